@@ -1,0 +1,148 @@
+"""ORACLE -- test infrastructure only.
+
+A plain fp64 CPU statement of the retrieve-and-inject path (oracle.c), with
+ctypes wrappers.  Only the tests, the smoke check and the bench's CPU-baseline
+leg use it; the GPU library neither imports nor links it, and it shares no
+code with the library.
+
+What each function follows ("InferScale: GPU-Native KV Injection for
+Personalized LLM Serving", gist.science explainer, technical summary):
+  rope_freqs, rotate   Online phase, dynamic rotation of stored pre-RoPE keys
+                       (textbook RoPE, rotate-half; Llama-3.1 scaling rule)
+  positions            Online phase, facts composed into one contiguous
+                       segment (after the request's prefix)
+  inject               Online phase, scatter-copy into the paged KV cache
+  topk                 Contributions, GPU-resident retrieval (exact
+                       inner-product top-k stands in for the index)
+Every function is pinned by tests/test_oracle_pins.py against closed forms,
+invariants, library routines and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# ORACLE_SO points the wrapper at another build (the mutant tests use it).
+SO = os.environ.get("ORACLE_SO") or os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+SCALING = {"none": 0, "llama3": 1}
+
+
+def build() -> None:
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           os.path.join(_HERE, "oracle.c"), "-o", SO, "-lm"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"oracle build failed:\n{r.stderr}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(SO):
+            build()
+        L = ctypes.CDLL(SO)
+        c = ctypes
+        L.or_half_to_double.argtypes = [c.c_uint16]
+        L.or_half_to_double.restype = c.c_double
+        L.or_double_to_bf16.argtypes = [c.c_double]
+        L.or_double_to_bf16.restype = c.c_uint16
+        L.or_llama3_scale.argtypes = [c.c_double] * 5
+        L.or_llama3_scale.restype = c.c_double
+        L.or_rope_freqs.argtypes = [c.c_int, c.c_double, c.c_int, c.c_double,
+                                    c.c_double, c.c_double, c.c_double, c.c_void_p]
+        L.or_rotate.argtypes = [c.c_void_p, c.c_int, c.c_double, c.c_void_p,
+                                c.c_void_p]
+        L.or_topk.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int64,
+                              c.c_int, c.c_void_p, c.c_void_p]
+        L.or_topk.restype = c.c_int
+        L.or_positions.argtypes = [c.c_int] + [c.c_void_p] * 5
+        L.or_inject.argtypes = ([c.c_int] * 4 + [c.c_void_p] * 3 + [c.c_int64, c.c_int]
+                                + [c.c_void_p] * 4 + [c.c_int, c.c_int, c.c_int64]
+                                + [c.c_void_p] * 2 + [c.c_int64] * 4 + [c.c_void_p])
+        L.or_inject.restype = c.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def half_to_double(bits: int) -> float:
+    return lib().or_half_to_double(bits)
+
+
+def double_to_bf16(x: float) -> int:
+    return lib().or_double_to_bf16(x)
+
+
+def llama3_scale(f: float, factor=8.0, low=1.0, high=4.0, orig=8192.0) -> float:
+    return lib().or_llama3_scale(f, factor, low, high, orig)
+
+
+def rope_freqs(d: int, theta: float, scaling: str = "none", factor=8.0, low=1.0,
+               high=4.0, orig=8192.0) -> np.ndarray:
+    out = np.empty(d // 2, dtype=np.float64)
+    lib().or_rope_freqs(d, theta, SCALING[scaling], factor, low, high, orig, _p(out))
+    return out
+
+
+def rotate(x: np.ndarray, p: float, freqs: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    f = np.ascontiguousarray(freqs, dtype=np.float64)
+    y = np.empty_like(x)
+    lib().or_rotate(_p(x), len(x), float(p), _p(f), _p(y))
+    return y
+
+
+def topk(q_bits: np.ndarray, e_bits: np.ndarray, k: int):
+    q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    e = np.ascontiguousarray(e_bits, dtype=np.uint16)
+    n_q, dim = q.shape
+    n_f = e.shape[0]
+    assert e.shape[1] == dim
+    ids = np.empty((n_q, k), dtype=np.int32)
+    scores = np.empty((n_q, k), dtype=np.float64)
+    if lib().or_topk(_p(q), _p(e), n_q, n_f, dim, k, _p(ids), _p(scores)) != 0:
+        raise ValueError("bad top-k arguments")
+    return ids, scores
+
+
+def positions(req_off, fact_ids, fact_len, prefix) -> np.ndarray:
+    req_off = np.ascontiguousarray(req_off, dtype=np.int32)
+    fact_ids = np.ascontiguousarray(fact_ids, dtype=np.int32)
+    fact_len = np.ascontiguousarray(fact_len, dtype=np.int32)
+    prefix = np.ascontiguousarray(prefix, dtype=np.int32)
+    start = np.empty(len(fact_ids), dtype=np.int64)
+    lib().or_positions(len(prefix), _p(req_off), _p(fact_ids), _p(fact_len),
+                       _p(prefix), _p(start))
+    return start
+
+
+def inject(n_layers, n_heads, d, dtype, k_store, v_store, tok_off, req_off, fact_ids,
+           prefix, block_tables, block_size, n_blocks, k_cache, v_cache, strides,
+           freqs) -> None:
+    """Writes into the host caches k_cache / v_cache (numpy, modified in
+    place).  strides = (layer, block, slot, head) in elements."""
+    tok_off = np.ascontiguousarray(tok_off, dtype=np.int64)
+    req_off = np.ascontiguousarray(req_off, dtype=np.int32)
+    fact_ids = np.ascontiguousarray(fact_ids, dtype=np.int32)
+    prefix = np.ascontiguousarray(prefix, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    f = np.ascontiguousarray(freqs, dtype=np.float64)
+    rc = lib().or_inject(n_layers, n_heads, d, dtype, _p(k_store), _p(v_store),
+                         _p(tok_off), len(tok_off) - 1, len(prefix), _p(req_off),
+                         _p(fact_ids), _p(prefix), _p(bt), bt.shape[1], block_size,
+                         n_blocks, _p(k_cache), _p(v_cache), *strides, _p(f))
+    if rc != 0:
+        raise ValueError("oracle inject: index out of range")
