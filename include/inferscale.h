@@ -1,0 +1,237 @@
+/*
+ * inferscale.h -- C ABI of the retrieve-and-inject hot path on MI355X (gfx950).
+ *
+ * The operations follow "InferScale: GPU-Native KV Injection for
+ * Personalized LLM Serving" (gist.science explainer pages, technical
+ * summary):
+ *   - the fact store holds, per fact, the keys captured before RoPE and the
+ *     raw values ("Online phase", pre-RoPE storage), here laid out
+ *     [fact][layer][kv_head][token][head_dim];
+ *   - retrieval runs over a GPU-resident index ("Contributions", GPU-native
+ *     system design); here an exact inner-product top-k over fp16 fact
+ *     embeddings stands in for the pages' index;
+ *   - the selected facts are composed into one contiguous segment, each
+ *     stored key is re-rotated to its new serving position ("Online phase",
+ *     dynamic rotation, Theorem 6) and the K/V are scatter-copied into the
+ *     serving engine's paged KV cache ("Online phase", injection);
+ *   - a store larger than GPU memory keeps part of its facts in host memory
+ *     ("Results", scalability: offload of the KV store to host DRAM).
+ * Readings where the pages are silent: textbook RoPE with frequencies
+ * theta^(-2i/d), rotate-half pairing (i, i + d/2), optional Llama-3.1
+ * frequency scaling; facts back to back in the caller's order right after
+ * the request's prefix; RoPE uses the logical position, not the slot.
+ *
+ * Conventions for every call:
+ *   - returns IS_OK (0) or a negative is_status; is_last_error() describes
+ *     the last failure of the calling thread;
+ *   - "host" pointers are read during the call only; "device" pointers must
+ *     stay valid until the work enqueued on `stream` has completed;
+ *   - `stream` is a hipStream_t (NULL = the default stream);
+ *   - validation completes before anything is enqueued: on error nothing
+ *     is written anywhere (all or nothing).
+ */
+#ifndef INFERSCALE_H
+#define INFERSCALE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IS_OK = 0,
+  IS_ERR_INVALID_ARG = -1,  /* null pointer, bad size or count           */
+  IS_ERR_FACT_ID = -2,      /* fact id outside [0, n_facts)              */
+  IS_ERR_BLOCK_TABLE = -3,  /* block table too short or entry out of range */
+  IS_ERR_SLOT_OVERLAP = -4, /* two injected tokens map to one cache slot */
+  IS_ERR_DTYPE = -5,        /* cache dtype differs from the store's      */
+  IS_ERR_ALIGN = -6,        /* pointer or stride breaks 16-byte rows     */
+  IS_ERR_OOM = -7,          /* device or pinned-host allocation failed   */
+  IS_ERR_HIP = -8,          /* a HIP runtime call failed                 */
+  IS_ERR_UNSUPPORTED = -9   /* valid, but outside what the kernels cover */
+} is_status;
+
+typedef enum { IS_DTYPE_F32 = 0, IS_DTYPE_BF16 = 1 } is_dtype;
+
+typedef enum { IS_ROPE_NONE = 0, IS_ROPE_LLAMA3 = 1 } is_rope_scaling;
+
+typedef struct is_store is_store;
+
+/*
+ * Store description (all host memory, read during is_store_create only).
+ *   n_layers, n_kv_heads, head_dim   K/V geometry; head_dim * element size
+ *                                    must be a multiple of 32 bytes (two
+ *                                    16-byte halves); head_dim/2 split into
+ *                                    16-byte chunks of 2, 4, 8, 16 or 32
+ *                                    lanes (bf16: head_dim 32..512, fp32:
+ *                                    16..256, powers of two)
+ *   kv_dtype                         is_dtype of stored K/V (and the cache)
+ *   n_facts, fact_len[n_facts]       number of facts and their token counts
+ *                                    (each >= 1)
+ *   emb_dim                          fp16 embedding width (multiple of 32),
+ *                                    0 = the store has no index (no top-k)
+ *   hbm_budget_bytes                 device bytes allowed for K+V; facts are
+ *                                    placed in id order in HBM while they
+ *                                    fit, the rest in pinned host memory;
+ *                                    < 0 means no limit
+ *   k_src, v_src                     optional host sources, every fact's
+ *                                    [layer][kv_head][token][head_dim] block
+ *                                    back to back in id order (NULL: leave
+ *                                    uninitialised, fill with is_store_load)
+ *   emb_src                          optional host [n_facts][emb_dim] fp16
+ */
+typedef struct {
+  int32_t n_layers;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dtype;
+  int64_t n_facts;
+  const int32_t* fact_len;
+  int32_t emb_dim;
+  int32_t reserved0;
+  int64_t hbm_budget_bytes;
+  const void* k_src;
+  const void* v_src;
+  const uint16_t* emb_src;
+} is_store_desc;
+
+/*
+ * Paged KV cache owned by the caller (the serving engine), in device
+ * memory.  Element (layer l, block b, slot s, kv_head h, dim i) of the K
+ * cache is k_base[l*stride_layer + b*stride_block + s*stride_slot +
+ * h*stride_head + i]; the same strides apply to v_base.  head_dim is
+ * contiguous.  Strides are in elements; every row start must be 16-byte
+ * aligned.  NHD layout [layer][block][slot][head][dim] and HND layout
+ * [layer][block][head][slot][dim] are both expressible.
+ */
+typedef struct {
+  void* k_base;
+  void* v_base;
+  int64_t stride_layer;
+  int64_t stride_block;
+  int64_t stride_slot;
+  int64_t stride_head;
+  int32_t block_size;
+  int32_t dtype;
+  int64_t n_blocks;
+} is_cache;
+
+/*
+ * RoPE parameters: frequencies theta^(-2i/head_dim), i < head_dim/2, and,
+ * for IS_ROPE_LLAMA3, the Llama-3.1 rule: wavelengths below
+ * orig_max_pos/high_freq_factor are kept, above orig_max_pos/low_freq_factor
+ * divided by `factor`, blended linearly in between.
+ */
+typedef struct {
+  double theta;
+  int32_t scaling;
+  int32_t reserved0;
+  double factor;
+  double low_freq_factor;
+  double high_freq_factor;
+  double orig_max_pos;
+} is_rope;
+
+/* Placement summary of a store. */
+typedef struct {
+  int64_t n_facts;
+  int64_t n_hbm_facts;       /* facts [0, n_hbm_facts) live in HBM         */
+  int64_t hbm_kv_bytes;      /* device bytes of K+V                        */
+  int64_t host_kv_bytes;     /* pinned host bytes of K+V                   */
+  int64_t total_tokens;
+  int64_t emb_bytes;
+} is_store_info;
+
+/*
+ * Creates a store: allocates device memory for the facts that fit the HBM
+ * budget (and pinned host memory for the rest) plus the fp16 embedding
+ * matrix, and copies the optional sources.  The library owns the memory;
+ * the caller may free its sources when the call returns.  Synchronous.
+ * Errors: IS_ERR_INVALID_ARG (geometry, lengths), IS_ERR_UNSUPPORTED
+ * (head_dim or emb_dim outside the kernels' shapes), IS_ERR_OOM.  Nothing
+ * stays allocated on error; *out is set only on success.
+ */
+int is_store_create(const is_store_desc* desc, is_store** out);
+
+/*
+ * Fills facts [first_fact, first_fact + n_facts) from K/V sources laid out
+ * like the store (those facts' blocks back to back) and, when emb is not
+ * NULL, their embedding rows.  src_on_device = 1 means the sources are
+ * device pointers.  Synchronous.  For stores larger than host memory the
+ * caller loads in chunks.  k or v may be NULL to skip that tensor.
+ * Errors: IS_ERR_INVALID_ARG (range), IS_ERR_HIP.
+ */
+int is_store_load(is_store* s, int64_t first_fact, int64_t n_facts,
+                  const void* k, const void* v, const uint16_t* emb,
+                  int src_on_device);
+
+/* Placement summary.  Errors: IS_ERR_INVALID_ARG. */
+int is_store_get_info(const is_store* s, is_store_info* out);
+
+/*
+ * Exact top-k inner-product search: for each query q (device
+ * q_f16[n_q][emb_dim], fp16 bits) the k facts with the largest
+ * <q, E[f]> (fp16 products, fp32 accumulation on the matrix cores), written
+ * to device ids[n_q][k] (int32) and scores[n_q][k] (fp32) in order of score
+ * descending, ties to the lower id.  Requires 1 <= k <= min(64, n_facts)
+ * and an embedding index.  Asynchronous on `stream`.
+ * Errors: IS_ERR_INVALID_ARG, IS_ERR_UNSUPPORTED (k > 64, no index),
+ * IS_ERR_OOM, IS_ERR_HIP.
+ */
+int is_topk(const is_store* s, const uint16_t* q_f16, int32_t n_q, int32_t k,
+            int32_t* ids, float* scores, void* stream);
+
+/*
+ * Retrieve-and-inject for a batch of requests.
+ *   req_off[n_req+1]   host; request r uses fact_ids[req_off[r]..req_off[r+1])
+ *   fact_ids[]         host; facts in segment order (a repeat is allowed and
+ *                      is injected twice)
+ *   prefix_len[n_req]  host; tokens already in the cache before the segment
+ *   block_tables       host [n_req][max_blocks]; physical block ids
+ * Request r's facts occupy serving positions prefix_len[r] .. prefix_len[r]
+ * + T_r - 1 back to back; the token at position p goes to slot
+ * block_tables[r][p / block_size] * block_size + p % block_size.  Its
+ * stored pre-RoPE key is rotated to position p (fp32 arithmetic, one
+ * rounding to the cache dtype) and written with its raw value to that slot;
+ * no other cache element is written.
+ * Validation (all before any work is enqueued): ids in range, every block
+ * table entry used in [0, n_blocks), block tables long enough, no two
+ * injected tokens of the call share a slot, cache dtype equals the store's,
+ * 16-byte row alignment, positions below 2^24.  Host arrays are copied
+ * before return; the kernels run asynchronously on `stream`.
+ * Errors: IS_ERR_INVALID_ARG, IS_ERR_FACT_ID, IS_ERR_BLOCK_TABLE,
+ * IS_ERR_SLOT_OVERLAP, IS_ERR_DTYPE, IS_ERR_ALIGN, IS_ERR_OOM, IS_ERR_HIP.
+ */
+int is_inject(const is_store* s, int32_t n_req, const int32_t* req_off,
+              const int32_t* fact_ids, const int32_t* prefix_len,
+              const int32_t* block_tables, int32_t max_blocks,
+              const is_cache* cache, const is_rope* rope, void* stream);
+
+/*
+ * The host half of is_inject on its own: validation and composition
+ * against a store description (no store, no GPU).  Returns the status
+ * is_inject would return for the same arguments before any device work,
+ * and the number of tokens that would be injected in *n_tokens (may be
+ * NULL).  The cache pointers are checked for alignment only.
+ */
+int is_inject_check(const is_store_desc* desc, int32_t n_req,
+                    const int32_t* req_off, const int32_t* fact_ids,
+                    const int32_t* prefix_len, const int32_t* block_tables,
+                    int32_t max_blocks, const is_cache* cache,
+                    const is_rope* rope, int64_t* n_tokens);
+
+/*
+ * Frees the store's device and host memory.  The caller must have
+ * completed all streams that use it.  NULL is a no-op.
+ */
+int is_store_destroy(is_store* s);
+
+/* Description of the calling thread's last error (empty if none). */
+const char* is_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFERSCALE_H */

@@ -1,0 +1,388 @@
+// C ABI of the library (include/inferscale.h): store placement in HBM and
+// pinned host memory, per-call staging of control data, kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "inferscale.h"
+#include "kernels.h"
+#include "plan.h"
+
+#define IS_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace is {
+const char* last_error_text();
+}
+
+namespace {
+
+using is::fail;
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(IS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// One slot of the per-store staging ring: a device buffer, its pinned host
+// mirror, and an event marking the end of the last work that used them.
+struct Slot {
+  void* dev = nullptr;
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+};
+
+constexpr int kSlots = 4;
+
+}  // namespace
+
+struct is_store {
+  int device = 0;
+  int32_t L = 0, H = 0, d = 0, dtype = 0, emb_dim = 0;
+  int64_t n_facts = 0, n_hbm = 0;
+  std::vector<int32_t> len;
+  std::vector<int64_t> tok_off;   // [n_facts + 1]
+  size_t es = 0;
+  void* k_dev = nullptr;
+  void* v_dev = nullptr;
+  void* k_host = nullptr;         // pinned, mapped
+  void* v_host = nullptr;
+  void* k_host_dev = nullptr;     // device aliases of the pinned arenas
+  void* v_host_dev = nullptr;
+  uint16_t* emb = nullptr;
+  std::mutex mu;
+  Slot slots[kSlots];
+  int next_slot = 0;
+
+  int64_t row_elems() const { return (int64_t)L * H * d; }
+  size_t fact_bytes(int64_t f0, int64_t f1) const {
+    return (size_t)(tok_off[f1] - tok_off[f0]) * row_elems() * es;
+  }
+  // Address of fact f's block in its arena (host pointer for host facts).
+  char* k_at(int64_t f) const {
+    return f < n_hbm ? (char*)k_dev + fact_bytes(0, f) : (char*)k_host + fact_bytes(n_hbm, f);
+  }
+  char* v_at(int64_t f) const {
+    return f < n_hbm ? (char*)v_dev + fact_bytes(0, f) : (char*)v_host + fact_bytes(n_hbm, f);
+  }
+};
+
+namespace {
+
+void free_store(is_store* s) {
+  if (s == nullptr) return;
+  DeviceGuard g(s->device);
+  for (Slot& sl : s->slots) {
+    if (sl.done) (void)hipEventSynchronize(sl.done);
+    if (sl.dev) (void)hipFree(sl.dev);
+    if (sl.host) (void)hipHostFree(sl.host);
+    if (sl.done) (void)hipEventDestroy(sl.done);
+  }
+  if (s->k_dev) (void)hipFree(s->k_dev);
+  if (s->v_dev) (void)hipFree(s->v_dev);
+  if (s->k_host) (void)hipHostFree(s->k_host);
+  if (s->v_host) (void)hipHostFree(s->v_host);
+  if (s->emb) (void)hipFree(s->emb);
+  delete s;
+}
+
+// Takes the next staging slot with room for `bytes`, after the work that
+// last used it has finished.  Caller holds s->mu.
+int acquire_slot(is_store* s, size_t bytes, Slot** out) {
+  Slot& sl = s->slots[s->next_slot];
+  s->next_slot = (s->next_slot + 1) % kSlots;
+  hipError_t e;
+  if (sl.done == nullptr) {
+    if ((e = hipEventCreateWithFlags(&sl.done, hipEventDisableTiming)) != hipSuccess)
+      return hip_fail(e, "hipEventCreate");
+  } else if ((e = hipEventSynchronize(sl.done)) != hipSuccess) {
+    return hip_fail(e, "hipEventSynchronize");
+  }
+  if (sl.cap < bytes) {
+    if (sl.dev) (void)hipFree(sl.dev);
+    if (sl.host) (void)hipHostFree(sl.host);
+    sl.dev = sl.host = nullptr;
+    sl.cap = 0;
+    const size_t cap = std::max<size_t>(bytes + bytes / 4, 1 << 16);
+    if (hipMalloc(&sl.dev, cap) != hipSuccess) return fail(IS_ERR_OOM, "staging hipMalloc");
+    if (hipHostMalloc(&sl.host, cap, hipHostMallocDefault) != hipSuccess) {
+      (void)hipFree(sl.dev);
+      sl.dev = nullptr;
+      return fail(IS_ERR_OOM, "staging hipHostMalloc");
+    }
+    sl.cap = cap;
+  }
+  *out = &sl;
+  return IS_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+is::StoreGeom geom_of(const is_store* s) {
+  is::StoreGeom g;
+  g.n_layers = s->L;
+  g.n_kv_heads = s->H;
+  g.head_dim = s->d;
+  g.dtype = s->dtype;
+  g.n_facts = s->n_facts;
+  g.fact_len = s->len.data();
+  g.tok_off = s->tok_off.data();
+  g.n_hbm = s->n_hbm;
+  return g;
+}
+
+}  // namespace
+
+IS_EXPORT const char* is_last_error(void) { return is::last_error_text(); }
+
+IS_EXPORT int is_store_create(const is_store_desc* d, is_store** out) {
+  is::clear_error();
+  if (out == nullptr) return fail(IS_ERR_INVALID_ARG, "null output handle");
+  int rc = is::check_store_desc(d);
+  if (rc != IS_OK) return rc;
+  is_store* s = new is_store();
+  if (hipGetDevice(&s->device) != hipSuccess) {
+    delete s;
+    return fail(IS_ERR_HIP, "no HIP device");
+  }
+  s->L = d->n_layers;
+  s->H = d->n_kv_heads;
+  s->d = d->head_dim;
+  s->dtype = d->kv_dtype;
+  s->emb_dim = d->emb_dim;
+  s->n_facts = d->n_facts;
+  s->es = (size_t)is::elem_size(d->kv_dtype);
+  s->len.assign(d->fact_len, d->fact_len + d->n_facts);
+  s->tok_off.assign((size_t)d->n_facts + 1, 0);
+  for (int64_t f = 0; f < d->n_facts; ++f) s->tok_off[f + 1] = s->tok_off[f] + s->len[f];
+  // Facts in id order go to HBM while K+V fit the budget.
+  const size_t per_tok = (size_t)s->row_elems() * s->es * 2;
+  if (d->hbm_budget_bytes < 0) {
+    s->n_hbm = s->n_facts;
+  } else {
+    const int64_t max_tok = (int64_t)((size_t)d->hbm_budget_bytes / per_tok);
+    s->n_hbm = std::upper_bound(s->tok_off.begin(), s->tok_off.end(), max_tok) -
+               s->tok_off.begin() - 1;
+  }
+  const size_t hbm_bytes = s->fact_bytes(0, s->n_hbm);
+  const size_t host_bytes = s->fact_bytes(s->n_hbm, s->n_facts);
+  if (hbm_bytes > 0 && (hipMalloc(&s->k_dev, hbm_bytes) != hipSuccess ||
+                        hipMalloc(&s->v_dev, hbm_bytes) != hipSuccess)) {
+    free_store(s);
+    return fail(IS_ERR_OOM, "device allocation of the fact store failed");
+  }
+  if (host_bytes > 0) {
+    if (hipHostMalloc(&s->k_host, host_bytes, hipHostMallocMapped) != hipSuccess ||
+        hipHostMalloc(&s->v_host, host_bytes, hipHostMallocMapped) != hipSuccess) {
+      free_store(s);
+      return fail(IS_ERR_OOM, "pinned host allocation of the fact store failed");
+    }
+    if (hipHostGetDevicePointer(&s->k_host_dev, s->k_host, 0) != hipSuccess ||
+        hipHostGetDevicePointer(&s->v_host_dev, s->v_host, 0) != hipSuccess) {
+      free_store(s);
+      return fail(IS_ERR_HIP, "hipHostGetDevicePointer failed");
+    }
+  }
+  if (s->emb_dim > 0 &&
+      hipMalloc((void**)&s->emb, (size_t)s->n_facts * s->emb_dim * 2) != hipSuccess) {
+    free_store(s);
+    return fail(IS_ERR_OOM, "device allocation of the embeddings failed");
+  }
+  if (d->k_src || d->v_src || d->emb_src) {
+    rc = is_store_load(s, 0, s->n_facts, d->k_src, d->v_src, d->emb_src, 0);
+    if (rc != IS_OK) {
+      std::string msg = is::last_error_text();
+      free_store(s);
+      return fail(rc, msg);
+    }
+  }
+  *out = s;
+  return IS_OK;
+}
+
+IS_EXPORT int is_store_load(is_store* s, int64_t first, int64_t n, const void* k,
+                            const void* v, const uint16_t* emb, int src_on_device) {
+  is::clear_error();
+  if (s == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  if (first < 0 || n < 0 || first + n > s->n_facts)
+    return fail(IS_ERR_INVALID_ARG, "fact range outside the store");
+  if (emb != nullptr && s->emb_dim == 0)
+    return fail(IS_ERR_INVALID_ARG, "store has no embedding index");
+  if (n == 0) return IS_OK;
+  DeviceGuard guard(s->device);
+  const hipMemcpyKind from_dev = src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  const hipMemcpyKind from_dev_to_host = src_on_device ? hipMemcpyDeviceToHost : hipMemcpyHostToHost;
+  const int64_t end = first + n;
+  // HBM part, then host part; each a contiguous span of the sources.
+  struct Part { int64_t f0, f1; bool host; };
+  const Part parts[2] = {{first, std::min(end, s->n_hbm), false},
+                         {std::max(first, s->n_hbm), end, true}};
+  size_t src_off = 0;
+  for (const Part& p : parts) {
+    if (p.f1 <= p.f0) continue;
+    const size_t bytes = s->fact_bytes(p.f0, p.f1);
+    const hipMemcpyKind kind = p.host ? from_dev_to_host : from_dev;
+    hipError_t e;
+    if (k && (e = hipMemcpy(s->k_at(p.f0), (const char*)k + src_off, bytes, kind)) != hipSuccess)
+      return hip_fail(e, "K load");
+    if (v && (e = hipMemcpy(s->v_at(p.f0), (const char*)v + src_off, bytes, kind)) != hipSuccess)
+      return hip_fail(e, "V load");
+    src_off += bytes;
+  }
+  if (emb) {
+    hipError_t e = hipMemcpy(s->emb + first * s->emb_dim, emb, (size_t)n * s->emb_dim * 2, from_dev);
+    if (e != hipSuccess) return hip_fail(e, "embedding load");
+  }
+  return IS_OK;
+}
+
+IS_EXPORT int is_store_get_info(const is_store* s, is_store_info* out) {
+  is::clear_error();
+  if (s == nullptr || out == nullptr) return fail(IS_ERR_INVALID_ARG, "null argument");
+  out->n_facts = s->n_facts;
+  out->n_hbm_facts = s->n_hbm;
+  out->hbm_kv_bytes = (int64_t)s->fact_bytes(0, s->n_hbm) * 2;
+  out->host_kv_bytes = (int64_t)s->fact_bytes(s->n_hbm, s->n_facts) * 2;
+  out->total_tokens = s->tok_off[s->n_facts];
+  out->emb_bytes = (int64_t)s->n_facts * s->emb_dim * 2;
+  return IS_OK;
+}
+
+IS_EXPORT int is_store_destroy(is_store* s) {
+  is::clear_error();
+  free_store(s);
+  return IS_OK;
+}
+
+IS_EXPORT int is_inject_check(const is_store_desc* d, int32_t n_req, const int32_t* req_off,
+                              const int32_t* fact_ids, const int32_t* prefix_len,
+                              const int32_t* block_tables, int32_t max_blocks,
+                              const is_cache* cache, const is_rope* rope, int64_t* n_tokens) {
+  is::clear_error();
+  int rc = is::check_store_desc(d);
+  if (rc != IS_OK) return rc;
+  is::StoreGeom g;
+  g.n_layers = d->n_layers;
+  g.n_kv_heads = d->n_kv_heads;
+  g.head_dim = d->head_dim;
+  g.dtype = d->kv_dtype;
+  g.n_facts = d->n_facts;
+  g.fact_len = d->fact_len;
+  g.n_hbm = d->n_facts;
+  return is::plan_inject(g, n_req, req_off, fact_ids, prefix_len, block_tables, max_blocks,
+                         cache, rope, nullptr, n_tokens);
+}
+
+IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_off,
+                        const int32_t* fact_ids, const int32_t* prefix_len,
+                        const int32_t* block_tables, int32_t max_blocks, const is_cache* cache,
+                        const is_rope* rope, void* stream) {
+  is::clear_error();
+  if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  is_store* s = const_cast<is_store*>(cs);
+  thread_local std::vector<is::WorkItem> items;
+  thread_local std::vector<float> g;
+  int64_t n_tokens = 0;
+  int rc = is::plan_inject(geom_of(s), n_req, req_off, fact_ids, prefix_len, block_tables,
+                           max_blocks, cache, rope, &items, &n_tokens);
+  if (rc != IS_OK) return rc;
+  if (items.empty()) return IS_OK;
+  is::plan_rope(s->d, rope, &g);
+  const size_t items_bytes = align256(items.size() * sizeof(is::WorkItem));
+  const size_t bt_bytes = align256((size_t)n_req * max_blocks * sizeof(int32_t));
+  const size_t g_bytes = align256(g.size() * sizeof(float));
+  const size_t total = items_bytes + bt_bytes + g_bytes;
+  DeviceGuard guard(s->device);
+  std::lock_guard<std::mutex> lock(s->mu);
+  Slot* sl = nullptr;
+  rc = acquire_slot(s, total, &sl);
+  if (rc != IS_OK) return rc;
+  char* h = static_cast<char*>(sl->host);
+  std::memcpy(h, items.data(), items.size() * sizeof(is::WorkItem));
+  std::memcpy(h + items_bytes, block_tables, (size_t)n_req * max_blocks * sizeof(int32_t));
+  std::memcpy(h + items_bytes + bt_bytes, g.data(), g.size() * sizeof(float));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(sl->dev, sl->host, total, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "staging copy");
+  is::InjectLaunch a{};
+  char* dv = static_cast<char*>(sl->dev);
+  a.k_dev = s->k_dev;
+  a.v_dev = s->v_dev;
+  a.k_host = s->k_host_dev;
+  a.v_host = s->v_host_dev;
+  a.kc = cache->k_base;
+  a.vc = cache->v_base;
+  a.s_layer = cache->stride_layer;
+  a.s_block = cache->stride_block;
+  a.s_slot = cache->stride_slot;
+  a.s_head = cache->stride_head;
+  a.work = reinterpret_cast<const is::WorkItem*>(dv);
+  a.bt = reinterpret_cast<const int32_t*>(dv + items_bytes);
+  a.g = reinterpret_cast<const float2*>(dv + items_bytes + bt_bytes);
+  a.n_items = (int32_t)items.size();
+  a.max_blocks = max_blocks;
+  a.block_size = cache->block_size;
+  a.n_layers = s->L;
+  a.n_heads = s->H;
+  a.head_dim = s->d;
+  a.dtype = s->dtype;
+  a.lanes = is::inject_lanes(s->d, s->dtype);
+  e = is::launch_inject(a, st);
+  if (e != hipSuccess) return hip_fail(e, "inject launch");
+  e = hipEventRecord(sl->done, st);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return IS_OK;
+}
+
+IS_EXPORT int is_topk(const is_store* cs, const uint16_t* q, int32_t n_q, int32_t k,
+                      int32_t* ids, float* scores, void* stream) {
+  is::clear_error();
+  if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  is_store* s = const_cast<is_store*>(cs);
+  if (s->emb_dim == 0 || s->emb == nullptr)
+    return fail(IS_ERR_UNSUPPORTED, "store has no embedding index");
+  if (n_q < 0) return fail(IS_ERR_INVALID_ARG, "n_q < 0");
+  if (k < 1 || k > s->n_facts) return fail(IS_ERR_INVALID_ARG, "k must be in [1, n_facts]");
+  if (k > 64) return fail(IS_ERR_UNSUPPORTED, "k > 64");
+  if (n_q == 0) return IS_OK;
+  if (q == nullptr || ids == nullptr || scores == nullptr)
+    return fail(IS_ERR_INVALID_ARG, "null query or output pointer");
+  if (((uintptr_t)q & 15u) != 0) return fail(IS_ERR_ALIGN, "queries must be 16-byte aligned");
+  is::TopkLaunch a{};
+  a.emb = s->emb;
+  a.q = q;
+  a.n_facts = s->n_facts;
+  a.emb_dim = s->emb_dim;
+  a.n_q = n_q;
+  a.k = k;
+  a.n_wg = is::topk_workgroups(s->n_facts);
+  a.ids = ids;
+  a.scores = scores;
+  const size_t bytes = (size_t)n_q * a.n_wg * k * sizeof(uint64_t);
+  DeviceGuard guard(s->device);
+  std::lock_guard<std::mutex> lock(s->mu);
+  Slot* sl = nullptr;
+  int rc = acquire_slot(s, bytes, &sl);
+  if (rc != IS_OK) return rc;
+  a.partial = static_cast<uint64_t*>(sl->dev);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = is::launch_topk(a, st);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  e = hipEventRecord(sl->done, st);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return IS_OK;
+}

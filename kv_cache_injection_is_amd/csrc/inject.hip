@@ -1,0 +1,217 @@
+// Fused gather -> Chunked RoPE -> paged scatter (the injection kernel).
+//
+// Follows the "Online phase" of the InferScale explainer pages
+// ("InferScale: GPU-Native KV Injection for Personalized LLM Serving",
+// technical summary): stored pre-RoPE keys receive the RoPE rotation of
+// their new serving position (Theorem 6: exact under RoPE) and, with the raw
+// values, are scatter-copied into the paged KV cache.  Rotation reading:
+// rotate-half pairs (i, i + d/2) turn by p * f_i.
+//
+// Design (gfx950): one workgroup of 256 lanes per (selected fact, layer).
+// The fact's [kv_head][token][head_dim] block for that layer is contiguous
+// in the store, so the workgroup streams it with 16-byte loads.  A lane owns
+// one 16-byte chunk of the first half of a row and the matching chunk of the
+// second half, so the rotate-half partner of every element sits in its own
+// registers.  cos/sin of p * f_i are computed once per (token, frequency) in
+// fp32 registers -- no table in memory -- and shared through LDS by all
+// kv_heads of the layer.  The angle is reduced exactly in turns: with
+// g = f / 2pi split as hi + lo in fp32, p*hi is split into its rounded value
+// and its exact FMA error, the integer turns are dropped, and the remaining
+// fraction feeds a quadrant reduction and Taylor polynomials of degree 9
+// (sine) and 10 (cosine) on |y| <= pi/4.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace is {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float2 sincos_of_turns(int p, float ghi, float glo) {
+  // The reduction relies on each product being rounded where written:
+  // contracting p*ghi into the later subtraction would count its rounding
+  // error twice.
+#pragma clang fp contract(off)
+  const float pf = (float)p;                  // exact: p < 2^24
+  const float t = pf * ghi;
+  const float e = __builtin_fmaf(pf, ghi, -t);  // exact error of p*ghi
+  const float r = (t - __builtin_rintf(t)) + __builtin_fmaf(pf, glo, e);  // turns
+  const float x4 = r * 4.0f;                   // quarter turns, exact
+  const float q = __builtin_rintf(x4);
+  const float z = x4 - q;                      // exact, |z| <= 1/2
+  // y = z * pi/2 with pi/2 split in two floats
+  const float y = __builtin_fmaf(z, 1.57079637050628662109375f,
+                                 z * -4.37113900018624283e-8f);
+  const float y2 = y * y;
+  // Taylor series of sin and cos about 0, truncated after y^9 and y^10
+  // (remainders below 2e-9 on |y| <= pi/4).
+  const float sp = __builtin_fmaf(y2, __builtin_fmaf(y2, __builtin_fmaf(y2,
+                       2.75573192239858907e-6f, -1.98412698412698413e-4f),
+                       8.33333333333333333e-3f), -1.66666666666666667e-1f);
+  const float sy = __builtin_fmaf(y * y2, sp, y);
+  const float cp = __builtin_fmaf(y2, __builtin_fmaf(y2, __builtin_fmaf(y2,
+                       __builtin_fmaf(y2, -2.75573192239858907e-7f,
+                                      2.48015873015873016e-5f),
+                       -1.38888888888888889e-3f), 4.16666666666666667e-2f), -0.5f);
+  const float cy = __builtin_fmaf(y2, cp, 1.0f);
+  const int quadrant = ((int)q) & 3;
+  float c, s;
+  if (quadrant == 0) { c = cy; s = sy; }
+  else if (quadrant == 1) { c = -sy; s = cy; }
+  else if (quadrant == 2) { c = -cy; s = -sy; }
+  else { c = sy; s = -cy; }
+  return make_float2(c, s);
+}
+
+__device__ __forceinline__ u32x4 load16(const char* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void store16(char* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  const __bf16 x = (__bf16)a;   // round to nearest even
+  const __bf16 y = (__bf16)b;
+  return (unsigned)__builtin_bit_cast(unsigned short, x) |
+         ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+}
+
+// Rotates the pairs (lo[e], hi[e]) by cs[e]; ES = element size.  Vector
+// elements are copied to scalars before any bit reinterpretation (a bit
+// cast applied to a vector-element lvalue reads the wrong element).
+template <int ES>
+__device__ __forceinline__ void rotate_chunk(u32x4& lo, u32x4& hi, const float2* cs) {
+  u32x4 nlo, nhi;
+  if constexpr (ES == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned ua = lo[e], ub = hi[e];
+      const float a = __uint_as_float(ua);
+      const float b = __uint_as_float(ub);
+      const float2 r = cs[e];
+      nlo[e] = __float_as_uint(__builtin_fmaf(a, r.x, -(b * r.y)));
+      nhi[e] = __float_as_uint(__builtin_fmaf(b, r.x, a * r.y));
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const unsigned ua = lo[w], ub = hi[w];
+      const float a0 = __uint_as_float(ua << 16);
+      const float a1 = __uint_as_float(ua & 0xFFFF0000u);
+      const float b0 = __uint_as_float(ub << 16);
+      const float b1 = __uint_as_float(ub & 0xFFFF0000u);
+      const float2 r0 = cs[2 * w], r1 = cs[2 * w + 1];
+      const float y0 = __builtin_fmaf(a0, r0.x, -(b0 * r0.y));
+      const float y1 = __builtin_fmaf(a1, r1.x, -(b1 * r1.y));
+      const float z0 = __builtin_fmaf(b0, r0.x, a0 * r0.y);
+      const float z1 = __builtin_fmaf(b1, r1.x, a1 * r1.y);
+      nlo[w] = pack_bf16(y0, y1);
+      nhi[w] = pack_bf16(z0, z1);
+    }
+  }
+  lo = nlo;
+  hi = nhi;
+}
+
+template <int ES, int LPT>
+__global__ __launch_bounds__(kThreads) void inject_kernel(InjectLaunch a) {
+  constexpr int VEC = 16 / ES;                 // elements per 16-byte chunk
+  constexpr int HALF = LPT * VEC;              // head_dim / 2
+  constexpr int D = 2 * HALF;
+  constexpr int TC = (4096 / HALF) < 128 ? (4096 / HALF) : 128;  // tokens per pass
+  constexpr int ROWS = kThreads / LPT;         // rows per workgroup sweep
+  constexpr int U = 4;                         // rows in flight per lane
+
+  __shared__ float2 cs[TC * HALF];
+  __shared__ int64_t slot_off[TC];
+
+  const WorkItem w = a.work[blockIdx.x];
+  const int layer = blockIdx.y;
+  const int len = w.len;
+  const int64_t layer_off = (w.elem_off + (int64_t)layer * a.n_heads * len * D) * ES;
+  const char* __restrict__ ksrc =
+      static_cast<const char*>(w.tier ? a.k_host : a.k_dev) + layer_off;
+  const char* __restrict__ vsrc =
+      static_cast<const char*>(w.tier ? a.v_host : a.v_dev) + layer_off;
+  char* __restrict__ kc = static_cast<char*>(a.kc);
+  char* __restrict__ vc = static_cast<char*>(a.vc);
+  const int32_t* __restrict__ bt = a.bt + (int64_t)w.req * a.max_blocks;
+  const int tid = threadIdx.x;
+  const int chunk = tid % LPT;
+
+  for (int t0 = 0; t0 < len; t0 += TC) {
+    const int tc = min(TC, len - t0);
+    for (int idx = tid; idx < tc * HALF; idx += kThreads) {
+      const int t = idx / HALF, i = idx % HALF;
+      const float2 g = a.g[i];
+      cs[idx] = sincos_of_turns(w.pos + t0 + t, g.x, g.y);
+    }
+    for (int t = tid; t < tc; t += kThreads) {
+      const int p = w.pos + t0 + t;
+      const int64_t blk = bt[p / a.block_size];
+      slot_off[t] = (int64_t)layer * a.s_layer + blk * a.s_block +
+                    (int64_t)(p % a.block_size) * a.s_slot;
+    }
+    __syncthreads();
+    const int rows = a.n_heads * tc;
+    const float inv_tc = 1.0f / (float)tc;
+    for (int r0 = tid / LPT; r0 < rows; r0 += U * ROWS) {
+      u32x4 klo[U], khi[U], vlo[U], vhi[U];
+      int hh[U], tt[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * ROWS;
+        const int h = (int)(((float)r + 0.5f) * inv_tc);   // r / tc for r < 2^16
+        hh[u] = h;
+        tt[u] = r - h * tc;
+        if (r < rows) {
+          const int64_t e = ((int64_t)h * len + t0 + tt[u]) * D + chunk * VEC;
+          klo[u] = load16(ksrc + e * ES);
+          khi[u] = load16(ksrc + (e + HALF) * ES);
+          vlo[u] = load16(vsrc + e * ES);
+          vhi[u] = load16(vsrc + (e + HALF) * ES);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * ROWS;
+        if (r < rows) {
+          rotate_chunk<ES>(klo[u], khi[u], cs + tt[u] * HALF + chunk * VEC);
+          const int64_t dst = slot_off[tt[u]] + (int64_t)hh[u] * a.s_head + chunk * VEC;
+          store16(kc + dst * ES, klo[u]);
+          store16(kc + (dst + HALF) * ES, khi[u]);
+          store16(vc + dst * ES, vlo[u]);
+          store16(vc + (dst + HALF) * ES, vhi[u]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int ES>
+hipError_t launch_es(const InjectLaunch& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.n_items, (unsigned)a.n_layers);
+  switch (a.lanes) {
+#define IS_CASE(L) \
+    case L: hipLaunchKernelGGL((inject_kernel<ES, L>), grid, dim3(kThreads), 0, stream, a); break;
+    IS_CASE(2) IS_CASE(4) IS_CASE(8) IS_CASE(16) IS_CASE(32)
+#undef IS_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_inject(const InjectLaunch& a, hipStream_t stream) {
+  if (a.n_items == 0) return hipSuccess;
+  return a.dtype == IS_DTYPE_F32 ? launch_es<4>(a, stream) : launch_es<2>(a, stream);
+}
+
+}  // namespace is

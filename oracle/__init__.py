@@ -11,7 +11,7 @@ Personalized LLM Serving", gist.science explainer, technical summary):
                        (textbook RoPE, rotate-half; Llama-3.1 scaling rule)
   positions            Online phase, facts composed into one contiguous
                        segment (after the request's prefix)
-  inject               Online phase, scatter-copy into the paged KV cache
+  token_slots, inject  Online phase, scatter-copy into the paged KV cache
   topk                 Contributions, GPU-resident retrieval (exact
                        inner-product top-k stands in for the index)
 Every function is pinned by tests/test_oracle_pins.py against closed forms,
@@ -69,6 +69,10 @@ def lib() -> ctypes.CDLL:
                                 + [c.c_void_p] * 4 + [c.c_int, c.c_int, c.c_int64]
                                 + [c.c_void_p] * 2 + [c.c_int64] * 4 + [c.c_void_p])
         L.or_inject.restype = c.c_int
+        L.or_token_slots.argtypes = [c.c_int] + [c.c_void_p] * 5 + [c.c_int, c.c_int, c.c_void_p]
+        L.or_token_slots.restype = c.c_int64
+        L.or_dot.argtypes = [c.c_void_p, c.c_void_p, c.c_int64]
+        L.or_dot.restype = c.c_double
         _lib = L
     return _lib
 
@@ -127,6 +131,28 @@ def positions(req_off, fact_ids, fact_len, prefix) -> np.ndarray:
     lib().or_positions(len(prefix), _p(req_off), _p(fact_ids), _p(fact_len),
                        _p(prefix), _p(start))
     return start
+
+
+def token_slots(req_off, fact_ids, fact_len, prefix, block_tables, block_size) -> np.ndarray:
+    """Cache slot of every injected token, in segment order."""
+    req_off = np.ascontiguousarray(req_off, dtype=np.int32)
+    fact_ids = np.ascontiguousarray(fact_ids, dtype=np.int32)
+    fact_len = np.ascontiguousarray(fact_len, dtype=np.int32)
+    prefix = np.ascontiguousarray(prefix, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    n = int(fact_len[fact_ids].sum()) if len(fact_ids) else 0
+    out = np.empty(max(n, 1), dtype=np.int64)
+    got = lib().or_token_slots(len(prefix), _p(req_off), _p(fact_ids), _p(fact_len), _p(prefix),
+                               _p(bt), bt.shape[1], block_size, _p(out))
+    if got < 0:
+        raise ValueError("block table too short")
+    return out[:got]
+
+
+def dot(a_bits: np.ndarray, b_bits: np.ndarray) -> float:
+    a = np.ascontiguousarray(a_bits, dtype=np.uint16)
+    b = np.ascontiguousarray(b_bits, dtype=np.uint16)
+    return lib().or_dot(_p(a), _p(b), len(a))
 
 
 def inject(n_layers, n_heads, d, dtype, k_store, v_store, tok_off, req_off, fact_ids,

@@ -177,6 +177,35 @@ EXPORT void or_positions(int n_req, const int32_t* req_off,
   }
 }
 
+/* Cache slot of every injected token, request by request, fact by fact
+ * (segment order), token by token: slot = block_table[r][p / block_size] *
+ * block_size + p % block_size for serving position p.  Returns the number of
+ * tokens, or -1 if a block-table lookup falls outside [0, max_blocks). */
+EXPORT int64_t or_token_slots(int n_req, const int32_t* req_off,
+                              const int32_t* fact_ids, const int32_t* fact_len,
+                              const int32_t* prefix_len,
+                              const int32_t* block_tables, int max_blocks,
+                              int block_size, int64_t* slots) {
+  int64_t n = 0;
+  for (int r = 0; r < n_req; ++r) {
+    int64_t p = prefix_len[r];
+    for (int32_t j = req_off[r]; j < req_off[r + 1]; ++j)
+      for (int32_t t = 0; t < fact_len[fact_ids[j]]; ++t, ++p) {
+        if (p / block_size >= max_blocks) return -1;
+        slots[n++] = (int64_t)block_tables[(int64_t)r * max_blocks + p / block_size] *
+                         block_size + p % block_size;
+      }
+  }
+  return n;
+}
+
+/* Exact inner product of two fp16 rows, in fp64. */
+EXPORT double or_dot(const uint16_t* a, const uint16_t* b, int64_t dim) {
+  double s = 0.0;
+  for (int64_t i = 0; i < dim; ++i) s += or_half_to_double(a[i]) * or_half_to_double(b[i]);
+  return s;
+}
+
 /* ----------------------------------------------------------------- inject */
 
 static double load_elem(const void* base, int64_t i, int dtype) {

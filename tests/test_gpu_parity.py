@@ -1,0 +1,188 @@
+"""GPU parity through the C ABI against the fp64 oracle, at sizes the
+oracle finishes in seconds (several tiles, ragged tails).  Tolerances are
+stated in tests/harness.py."""
+import numpy as np
+import pytest
+
+import synth
+from synth import workloads as W
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_cleanup(gpu):
+    yield
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_smoke_tiny(gpu):
+    Hn.smoke()
+
+
+def _zipf_problem(w, n_req, k, seed_fact_count=None):
+    lens = W.fact_lengths(w)
+    ids = synth.zipf_requests(w.seed, n_req, k, w.n_facts, w.zipf_s)
+    req_off, flat = Hn.requests_from_ids(ids)
+    prefix = synth.prefixes(w.seed, n_req, w.prefix[0], w.prefix[1])
+    bt = Hn.block_tables_for(w, lens, req_off, flat, prefix)
+    return lens, req_off, flat, prefix, bt
+
+
+SMALL_LLAMA = W.WORKLOADS["llama8b_batch"].scaled(name="llama_small", n_facts=300, n_req=6,
+                                                  k=5, n_blocks=160, emb_dim=0)
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_inject_llama_shape_small(gpu, layout):
+    w = SMALL_LLAMA
+    Hn.log(f"inject llama-shaped small, layout {layout}")
+    lens, req_off, flat, prefix, bt = _zipf_problem(w, w.n_req, w.k)
+    st = Hn.make_store(w, lens)
+    try:
+        cache = Hn.make_cache(w, layout=layout)
+        Hn.gpu_inject(st, cache, req_off, flat, prefix, bt)
+        n, err = Hn.check_inject_blocks(cache, lens, req_off, flat, prefix, bt,
+                                        Hn.blocks_of(bt, range(w.n_req)))
+        Hn.log(f"  {n} K elements, max err {err:.3g}")
+        # blocks no request uses stay untouched
+        used = set(Hn.blocks_of(bt, range(w.n_req)).tolist())
+        free = np.array([b for b in range(w.n_blocks) if b not in used][:8])
+        Hn.check_inject_blocks(cache, lens, np.array([0, 0], np.int32), flat[:0],
+                               prefix[:1], bt[:1], free)
+    finally:
+        st.destroy()
+
+
+def test_inject_fp32_head128_and_repeat(gpu):
+    w = W.WORKLOADS["tiny"].scaled(name="f32_128", head_dim=128, n_layers=3, n_kv_heads=2,
+                                   n_facts=40, len_dist=("uniform", 1, 70), n_blocks=64,
+                                   emb_dim=0, theta=1e6)
+    lens = W.fact_lengths(w)
+    req_off = np.array([0, 3, 7], np.int32)
+    flat = np.array([5, 5, 39, 0, 1, 2, 3], np.int32)     # fact 5 twice in request 0
+    prefix = np.array([0, 131], np.int32)
+    bt = Hn.block_tables_for(w, lens, req_off, flat, prefix)
+    st = Hn.make_store(w, lens, fill="host")
+    try:
+        cache = Hn.make_cache(w)
+        Hn.gpu_inject(st, cache, req_off, flat, prefix, bt)
+        Hn.check_inject_blocks(cache, lens, req_off, flat, prefix, bt, np.arange(w.n_blocks))
+    finally:
+        st.destroy()
+
+
+def test_inject_host_tier(gpu):
+    """Facts beyond the HBM budget live in pinned host memory and are read
+    from there by the same kernel."""
+    w = SMALL_LLAMA.scaled(name="llama_offload", n_facts=120)
+    lens, req_off, flat, prefix, bt = _zipf_problem(w, 4, 8)
+    budget = int(lens[:60].sum()) * w.token_bytes * 2
+    st = Hn.make_store(w, lens, hbm_budget=budget)
+    try:
+        info = Hn.K.is_store_get_info(st.handle)
+        assert info.n_hbm_facts == 60 and info.host_kv_bytes > 0
+        assert (flat >= 60).any() and (flat < 60).any()
+        cache = Hn.make_cache(w)
+        Hn.gpu_inject(st, cache, req_off, flat, prefix, bt)
+        Hn.check_inject_blocks(cache, lens, req_off, flat, prefix, bt,
+                               Hn.blocks_of(bt, range(4)))
+    finally:
+        st.destroy()
+
+
+def test_inject_deterministic_and_position_zero_identity(gpu):
+    import torch
+    w = SMALL_LLAMA
+    lens, req_off, flat, prefix, bt = _zipf_problem(w, 3, 4)
+    prefix[:] = 0
+    bt = Hn.block_tables_for(w, lens, req_off, flat, prefix)
+    st = Hn.make_store(w, lens)
+    try:
+        c1 = Hn.make_cache(w)
+        c2 = Hn.make_cache(w)
+        Hn.gpu_inject(st, c1, req_off, flat, prefix, bt)
+        Hn.gpu_inject(st, c2, req_off, flat, prefix, bt)
+        torch.cuda.synchronize()
+        assert torch.equal(c1.k, c2.k) and torch.equal(c1.v, c2.v)
+        # the first token of request 0 sits at position 0: its K is the stored K
+        f = int(flat[0])
+        k_pre = synth.fact_kv(w.seed, synth.TAG_K, f, int(lens[f]) * w.row_elems, w.dtype)
+        k_pre = k_pre.reshape(w.n_layers, w.n_kv_heads, int(lens[f]), w.head_dim)[:, :, 0]
+        blk = int(bt[0, 0])
+        got = c1.k.view(w.n_layers, w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim * 2)
+        got = got[:, blk, 0].cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, k_pre)
+    finally:
+        st.destroy()
+
+
+def test_inject_invalid_call_writes_nothing(gpu):
+    import torch
+    w = SMALL_LLAMA
+    lens, req_off, flat, prefix, bt = _zipf_problem(w, 3, 4)
+    st = Hn.make_store(w, lens)
+    try:
+        cache = Hn.make_cache(w)
+        before = cache.k.clone()
+        bad = flat.copy()
+        bad[-1] = w.n_facts
+        with pytest.raises(Hn.K.ISError) as e:
+            Hn.gpu_inject(st, cache, req_off, bad, prefix, bt)
+        assert e.value.code == -2
+        # request 1 = request 0 with the same block table: every slot collides
+        k0 = req_off[1]
+        twice = np.concatenate([flat[:k0], flat[:k0]])
+        with pytest.raises(Hn.K.ISError) as e:
+            Hn.gpu_inject(st, cache, np.array([0, k0, 2 * k0], np.int32), twice,
+                          np.array([prefix[0], prefix[0]], np.int32), np.stack([bt[0], bt[0]]))
+        assert e.value.code == -4
+        torch.cuda.synchronize()
+        assert torch.equal(before, cache.k)
+    finally:
+        st.destroy()
+
+
+@pytest.mark.parametrize("n_facts,dim,n_q,k", [
+    (20, 32, 1, 5),          # tiny shape
+    (1000, 128, 7, 10),      # several tiles, ragged tail
+    (5003, 1024, 100, 50),   # 20 workgroups, the 100-query batch
+    (3000, 256, 130, 64),    # two query blocks, k at its maximum
+    (70000, 128, 3, 1),      # all 256 workgroups, several tiles each
+])
+def test_topk_parity(gpu, n_facts, dim, n_q, k):
+    w = W.WORKLOADS["tiny"].scaled(name="topk", n_facts=n_facts, emb_dim=dim, n_req=n_q,
+                                   len_dist=("uniform", 1, 2), seed=n_facts)
+    Hn.log(f"top-k parity: {n_facts} facts x {dim}, {n_q} queries, k={k}")
+    st = Hn.make_store(w, fill="host")
+    try:
+        q = W.query_embeddings(w)
+        ids, sc = Hn.gpu_topk(st, q, k)
+        Hn.check_topk(q, st.emb, ids, sc, k)
+        ids2, sc2 = Hn.gpu_topk(st, q, k)
+        assert np.array_equal(ids, ids2) and np.array_equal(sc, sc2)
+    finally:
+        st.destroy()
+
+
+def test_topk_ties_and_self_match(gpu):
+    w = W.WORKLOADS["tiny"].scaled(name="ties", n_facts=600, emb_dim=64, n_req=4,
+                                   len_dist=("uniform", 1, 1))
+    lens = W.fact_lengths(w)
+    emb = W.fact_embeddings(w)
+    emb[300] = emb[17]
+    emb[599] = emb[17]
+    desc, keep = Hn.K.make_desc(1, 2, 64, synth.F32, lens, 64, -1, None, None, emb)
+    h = Hn.K.is_store_create(desc)
+    st = Hn.Store(w, lens, np.concatenate([[0], np.cumsum(lens)]), h, emb)
+    try:
+        q = emb[[17, 5, 599, 42]]
+        ids, sc = Hn.gpu_topk(st, q, 3)
+        assert ids[0].tolist() == [17, 300, 599]
+        assert ids[2].tolist() == [17, 300, 599]
+        assert ids[1, 0] == 5 and ids[3, 0] == 42
+    finally:
+        st.destroy()

@@ -421,3 +421,32 @@ def test_theorem3_one_layer_attention_injection_equals_prefill():
         Vs.append(Wv @ emb[t])
         out.append(attend(Wq @ emb[t], p, np.stack(Ks), np.stack(Vs)))
     assert np.max(np.abs(np.array(out) - np.array(ref))) < 1e-9
+
+
+def test_token_slots_brute_force_walk():
+    P = _small_problem(synth.F32)
+    slots = oracle.token_slots(P["req_off"], P["ids"], P["lens"], P["prefix"], P["bt"], P["B"])
+    B = P["B"]
+    expect = []
+    for r in range(3):
+        blk_i, in_blk = 0, 0
+        for _ in range(int(P["prefix"][r])):
+            in_blk += 1
+            if in_blk == B:
+                blk_i, in_blk = blk_i + 1, 0
+        for j in range(P["req_off"][r], P["req_off"][r + 1]):
+            for _ in range(int(P["lens"][P["ids"][j]])):
+                expect.append(int(P["bt"][r][blk_i]) * B + in_blk)
+                in_blk += 1
+                if in_blk == B:
+                    blk_i, in_blk = blk_i + 1, 0
+    assert slots.tolist() == expect
+    assert len(set(expect)) == len(expect)
+
+
+def test_dot_exact_against_fractions():
+    a = synth.queries(5, 1, 64)[0]
+    b = synth.embeddings(5, 0, 1, 64)[0]
+    ref = sum(Fraction(float(x)) * Fraction(float(y)) for x, y in
+              zip(a.view(np.float16).astype(np.float64), b.view(np.float16).astype(np.float64)))
+    assert oracle.dot(a, b) == pytest.approx(float(ref), abs=1e-15)
