@@ -14,7 +14,8 @@ import os
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-SO = os.path.join(PKG, "libinferscale.so")
+# INFERSCALE_SO points the binding at another build of the library (tuning builds).
+SO = os.environ.get("INFERSCALE_SO") or os.path.join(PKG, "libinferscale.so")
 
 IS_OK = 0
 STATUS = {0: "IS_OK", -1: "IS_ERR_INVALID_ARG", -2: "IS_ERR_FACT_ID", -3: "IS_ERR_BLOCK_TABLE",

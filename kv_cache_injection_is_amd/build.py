@@ -16,18 +16,21 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-fvisibility=hi
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", f"-I{INCLUDE}"]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = SO, defines=()) -> str:
+    """Compiles the library to `out`; `defines` are extra -D tuning knobs."""
     objs = []
+    tag = os.path.basename(out).replace(".so", "")
     for src in SOURCES:
-        obj = os.path.join(CSRC, src + ".o")
+        obj = os.path.join(CSRC, f"{src}.{tag}.o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], *lang, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
-    _run([HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", *objs, "-o", SO], verbose)
+    _run([HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", *objs, "-o", out], verbose)
     for o in objs:
         os.remove(o)
-    return SO
+    return out
 
 
 def _run(cmd, verbose):

@@ -301,6 +301,15 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
                            max_blocks, cache, rope, &items, &n_tokens);
   if (rc != IS_OK) return rc;
   if (items.empty()) return IS_OK;
+#ifndef IS_SORT_WORK
+#define IS_SORT_WORK 1
+#endif
+#if IS_SORT_WORK
+  // Launch order only: workgroups then sweep the store in address order.
+  std::sort(items.begin(), items.end(), [](const is::WorkItem& x, const is::WorkItem& y) {
+    return x.tier != y.tier ? x.tier < y.tier : x.elem_off < y.elem_off;
+  });
+#endif
   is::plan_rope(s->d, rope, &g);
   const size_t items_bytes = align256(items.size() * sizeof(is::WorkItem));
   const size_t bt_bytes = align256((size_t)n_req * max_blocks * sizeof(int32_t));

@@ -23,6 +23,39 @@
 
 #include "kernels.h"
 
+// Tuning knobs (compile-time).
+#ifndef IS_INJECT_NT
+#define IS_INJECT_NT 1          // non-temporal loads of the store and stores to the cache
+#endif
+#ifndef IS_INJECT_PREFETCH
+#define IS_INJECT_PREFETCH 0    // issue the first rows' loads before computing cos/sin
+#endif
+#ifndef IS_INJECT_LDS_TABLE
+#define IS_INJECT_LDS_TABLE 32768   // bytes of the per-chunk cos/sin table
+#endif
+#ifndef IS_INJECT_ROWS
+#define IS_INJECT_ROWS 4        // rows in flight per lane
+#endif
+// Row-contiguous variant for 256-byte rows (bf16 head_dim 128, fp32 64).
+#ifndef IS_R16
+#define IS_R16 1                // use it where it applies
+#endif
+#ifndef IS_R16_THREADS
+#define IS_R16_THREADS 512
+#endif
+#ifndef IS_R16_LAYERS
+#define IS_R16_LAYERS 1         // layers per workgroup
+#endif
+#ifndef IS_R16_ROWS
+#define IS_R16_ROWS 8           // rows in flight per lane
+#endif
+#ifndef IS_R16_TC
+#define IS_R16_TC 64            // tokens per cos/sin pass
+#endif
+#ifndef IS_R16_LAYER_FAST
+#define IS_R16_LAYER_FAST 1     // grid x = layer group (consecutive workgroups share a fact)
+#endif
+
 namespace is {
 namespace {
 
@@ -67,11 +100,19 @@ __device__ __forceinline__ float2 sincos_of_turns(int p, float ghi, float glo) {
 }
 
 __device__ __forceinline__ u32x4 load16(const char* p) {
+#if IS_INJECT_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
   return *reinterpret_cast<const u32x4*>(p);
+#endif
 }
 
 __device__ __forceinline__ void store16(char* p, u32x4 v) {
+#if IS_INJECT_NT
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+#else
   *reinterpret_cast<u32x4*>(p) = v;
+#endif
 }
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
@@ -123,9 +164,10 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectLaunch a) {
   constexpr int VEC = 16 / ES;                 // elements per 16-byte chunk
   constexpr int HALF = LPT * VEC;              // head_dim / 2
   constexpr int D = 2 * HALF;
-  constexpr int TC = (4096 / HALF) < 128 ? (4096 / HALF) : 128;  // tokens per pass
+  constexpr int TC = (IS_INJECT_LDS_TABLE / 8 / HALF) < 128 ? (IS_INJECT_LDS_TABLE / 8 / HALF)
+                                                             : 128;  // tokens per pass
   constexpr int ROWS = kThreads / LPT;         // rows per workgroup sweep
-  constexpr int U = 4;                         // rows in flight per lane
+  constexpr int U = IS_INJECT_ROWS;            // rows in flight per lane
 
   __shared__ float2 cs[TC * HALF];
   __shared__ int64_t slot_off[TC];
@@ -146,23 +188,12 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectLaunch a) {
 
   for (int t0 = 0; t0 < len; t0 += TC) {
     const int tc = min(TC, len - t0);
-    for (int idx = tid; idx < tc * HALF; idx += kThreads) {
-      const int t = idx / HALF, i = idx % HALF;
-      const float2 g = a.g[i];
-      cs[idx] = sincos_of_turns(w.pos + t0 + t, g.x, g.y);
-    }
-    for (int t = tid; t < tc; t += kThreads) {
-      const int p = w.pos + t0 + t;
-      const int64_t blk = bt[p / a.block_size];
-      slot_off[t] = (int64_t)layer * a.s_layer + blk * a.s_block +
-                    (int64_t)(p % a.block_size) * a.s_slot;
-    }
-    __syncthreads();
     const int rows = a.n_heads * tc;
     const float inv_tc = 1.0f / (float)tc;
-    for (int r0 = tid / LPT; r0 < rows; r0 += U * ROWS) {
-      u32x4 klo[U], khi[U], vlo[U], vhi[U];
-      int hh[U], tt[U];
+    u32x4 klo[U], khi[U], vlo[U], vhi[U];
+    int hh[U], tt[U];
+    // Loads of rows r0 + u*ROWS, u < U (rows past `rows` are skipped).
+    auto load_rows = [&](int r0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int r = r0 + u * ROWS;
@@ -177,6 +208,29 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectLaunch a) {
           vhi[u] = load16(vsrc + (e + HALF) * ES);
         }
       }
+    };
+    int r0 = tid / LPT;
+#if IS_INJECT_PREFETCH
+    load_rows(r0);
+#endif
+    for (int idx = tid; idx < tc * HALF; idx += kThreads) {
+      const int t = idx / HALF, i = idx % HALF;
+      const float2 g = a.g[i];
+      cs[idx] = sincos_of_turns(w.pos + t0 + t, g.x, g.y);
+    }
+    for (int t = tid; t < tc; t += kThreads) {
+      const int p = w.pos + t0 + t;
+      const int64_t blk = bt[p / a.block_size];
+      slot_off[t] = (int64_t)layer * a.s_layer + blk * a.s_block +
+                    (int64_t)(p % a.block_size) * a.s_slot;
+    }
+    __syncthreads();
+    for (; r0 < rows; r0 += U * ROWS) {
+#if IS_INJECT_PREFETCH
+      if (r0 != tid / LPT) load_rows(r0);
+#else
+      load_rows(r0);
+#endif
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int r = r0 + u * ROWS;
@@ -194,8 +248,132 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectLaunch a) {
   }
 }
 
+// Row-contiguous injection for 256-byte rows: 16 lanes cover a row with one
+// 16-byte chunk each, so a wave's load or store covers four whole rows.  The
+// rotate-half partner of lane c (first half) is lane c + 8 (second half) of
+// the same 16-lane row; the pair swap is a DPP rotate by 8 within the row.
+// A workgroup handles G consecutive layers of one selected fact: those
+// layers' [kv_head][token][head_dim] blocks are one contiguous span.
+template <int ES, int T, int G, int U, int TC>
+__global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
+  constexpr int VEC = 16 / ES;      // elements per lane
+  constexpr int HALF = 8 * VEC;     // head_dim / 2
+  constexpr int D = 2 * HALF;
+  constexpr int RPS = T / 16;       // rows per workgroup sweep
+  __shared__ float2 cs[TC * HALF];
+  __shared__ int64_t slot_off[TC];
+
+#if IS_R16_LAYER_FAST
+  const WorkItem w = a.work[blockIdx.y];
+  const int l0 = blockIdx.x * G;
+#else
+  const WorkItem w = a.work[blockIdx.x];
+  const int l0 = blockIdx.y * G;
+#endif
+  const int nl = min(G, a.n_layers - l0);
+  const int len = w.len;
+  const int H = a.n_heads;
+  const int64_t base = (w.elem_off + (int64_t)l0 * H * len * D) * ES;
+  const char* __restrict__ ksrc = static_cast<const char*>(w.tier ? a.k_host : a.k_dev) + base;
+  const char* __restrict__ vsrc = static_cast<const char*>(w.tier ? a.v_host : a.v_dev) + base;
+  char* __restrict__ kc = static_cast<char*>(a.kc);
+  char* __restrict__ vc = static_cast<char*>(a.vc);
+  const int32_t* __restrict__ bt = a.bt + (int64_t)w.req * a.max_blocks;
+  const int tid = threadIdx.x;
+  const int c = tid & 15;
+  const int upper = c >> 3;                  // 0: first half of the row, 1: second
+  const int col = upper * HALF + (c & 7) * VEC;
+  const int fcol = (c & 7) * VEC;            // first frequency of this lane
+  const float sgn = upper ? 1.0f : -1.0f;
+
+  for (int t0 = 0; t0 < len; t0 += TC) {
+    const int tc = min(TC, len - t0);
+    for (int idx = tid; idx < tc * HALF; idx += T) {
+      const int t = idx / HALF, i = idx % HALF;
+      const float2 g = a.g[i];
+      cs[idx] = sincos_of_turns(w.pos + t0 + t, g.x, g.y);
+    }
+    for (int t = tid; t < tc; t += T) {
+      const int p = w.pos + t0 + t;
+      slot_off[t] = (int64_t)bt[p / a.block_size] * a.s_block +
+                    (int64_t)(p % a.block_size) * a.s_slot;
+    }
+    __syncthreads();
+    const int per_layer = H * tc;
+    const int rows = nl * per_layer;
+    const float inv_pl = 1.0f / (float)per_layer;
+    const float inv_tc = 1.0f / (float)tc;
+    for (int r0 = tid / 16; r0 < rows; r0 += U * RPS) {
+      u32x4 kv[U], vv[U];
+      int gl[U], hh[U], tt[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * RPS;
+        // r -> (layer g, head h, token t); exact for r < 2^16
+        const int g = (int)(((float)r + 0.5f) * inv_pl);
+        const int rem = r - g * per_layer;
+        const int h = (int)(((float)rem + 0.5f) * inv_tc);
+        gl[u] = g;
+        hh[u] = h;
+        tt[u] = rem - h * tc;
+        if (r < rows) {
+          const int64_t e = ((int64_t)(g * H + h) * len + t0 + tt[u]) * D + col;
+          kv[u] = load16(ksrc + e * ES);
+          vv[u] = load16(vsrc + e * ES);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * RPS;
+        if (r < rows) {   // uniform across each 16-lane row
+          u32x4 other;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            other[q] = (unsigned)__builtin_amdgcn_mov_dpp((int)kv[u][q], 0x128, 0xF, 0xF, false);
+          const float2* csr = cs + tt[u] * HALF + fcol;
+          u32x4 out;
+          if constexpr (ES == 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const unsigned uo = kv[u][e], up = other[e];
+              const float2 r2 = csr[e];
+              out[e] = __float_as_uint(__builtin_fmaf(__uint_as_float(uo), r2.x,
+                                                      __uint_as_float(up) * (sgn * r2.y)));
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const unsigned uo = kv[u][q], up = other[q];
+              const float2 r0c = csr[2 * q], r1c = csr[2 * q + 1];
+              const float y0 = __builtin_fmaf(__uint_as_float(uo << 16), r0c.x,
+                                              __uint_as_float(up << 16) * (sgn * r0c.y));
+              const float y1 = __builtin_fmaf(__uint_as_float(uo & 0xFFFF0000u), r1c.x,
+                                              __uint_as_float(up & 0xFFFF0000u) * (sgn * r1c.y));
+              out[q] = pack_bf16(y0, y1);
+            }
+          }
+          const int64_t dst = (int64_t)(l0 + gl[u]) * a.s_layer + slot_off[tt[u]] +
+                              (int64_t)hh[u] * a.s_head + col;
+          store16(kc + dst * ES, out);
+          store16(vc + dst * ES, vv[u]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int ES>
 hipError_t launch_es(const InjectLaunch& a, hipStream_t stream) {
+  if (IS_R16 && a.lanes == 8) {
+    constexpr int G = IS_R16_LAYERS;
+    const unsigned n_groups = (unsigned)((a.n_layers + G - 1) / G);
+    const dim3 grid16 = IS_R16_LAYER_FAST ? dim3(n_groups, (unsigned)a.n_items)
+                                          : dim3((unsigned)a.n_items, n_groups);
+    hipLaunchKernelGGL((inject_row16<ES, IS_R16_THREADS, G, IS_R16_ROWS, IS_R16_TC>), grid16,
+                       dim3(IS_R16_THREADS), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)a.n_items, (unsigned)a.n_layers);
   switch (a.lanes) {
 #define IS_CASE(L) \

@@ -75,6 +75,21 @@ def test_inject_fp32_head128_and_repeat(gpu):
         st.destroy()
 
 
+@pytest.mark.parametrize("dtype,head_dim", [(synth.BF16, 64), (synth.BF16, 256), (synth.F32, 32)])
+def test_inject_other_head_dims(gpu, dtype, head_dim):
+    """Shapes served by the general kernel (rows other than 256 bytes)."""
+    w = SMALL_LLAMA.scaled(name=f"hd{head_dim}", n_layers=3, n_kv_heads=4, head_dim=head_dim,
+                           dtype=dtype, n_facts=50, n_blocks=96, theta=1e4, scaling="none")
+    lens, req_off, flat, prefix, bt = _zipf_problem(w, 5, 6)
+    st = Hn.make_store(w, lens)
+    try:
+        cache = Hn.make_cache(w, layout="HND" if head_dim == 256 else "NHD")
+        Hn.gpu_inject(st, cache, req_off, flat, prefix, bt)
+        Hn.check_inject_blocks(cache, lens, req_off, flat, prefix, bt, np.arange(w.n_blocks))
+    finally:
+        st.destroy()
+
+
 def test_inject_host_tier(gpu):
     """Facts beyond the HBM budget live in pinned host memory and are read
     from there by the same kernel."""
