@@ -371,27 +371,37 @@ IS_EXPORT int is_topk(const is_store* cs, const uint16_t* q, int32_t n_q, int32_
   if (q == nullptr || ids == nullptr || scores == nullptr)
     return fail(IS_ERR_INVALID_ARG, "null query or output pointer");
   if (((uintptr_t)q & 15u) != 0) return fail(IS_ERR_ALIGN, "queries must be 16-byte aligned");
-  is::TopkLaunch a{};
-  a.emb = s->emb;
-  a.q = q;
-  a.n_facts = s->n_facts;
-  a.emb_dim = s->emb_dim;
-  a.n_q = n_q;
-  a.k = k;
-  a.n_wg = is::topk_workgroups(s->n_facts);
-  a.ids = ids;
-  a.scores = scores;
-  const size_t bytes = (size_t)n_q * a.n_wg * k * sizeof(uint64_t);
   DeviceGuard guard(s->device);
   std::lock_guard<std::mutex> lock(s->mu);
-  Slot* sl = nullptr;
-  int rc = acquire_slot(s, bytes, &sl);
-  if (rc != IS_OK) return rc;
-  a.partial = static_cast<uint64_t*>(sl->dev);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = is::launch_topk(a, st);
-  if (e != hipSuccess) return hip_fail(e, "top-k launch");
-  e = hipEventRecord(sl->done, st);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  // Queries go in groups of up to 128 (one query block per scan).
+  for (int32_t q0 = 0; q0 < n_q; q0 += 128) {
+    const int32_t nq = std::min<int32_t>(128, n_q - q0);
+    is::TopkLaunch a{};
+    a.emb = s->emb;
+    a.q = q + (int64_t)q0 * s->emb_dim;
+    a.n_facts = s->n_facts;
+    a.sample_n = is::topk_sample_size(s->n_facts);
+    a.emb_dim = s->emb_dim;
+    a.n_q = nq;
+    a.k = k;
+    a.ids = ids + (int64_t)q0 * k;
+    a.scores = scores + (int64_t)q0 * k;
+    Slot* sl = nullptr;
+    int rc = acquire_slot(s, is::topk_scratch_bytes(s->n_facts, nq), &sl);
+    if (rc != IS_OK) return rc;
+    char* p = static_cast<char*>(sl->dev);
+    a.sample = reinterpret_cast<float*>(p);
+    p += align256((size_t)nq * a.sample_n * 4);
+    a.tau = reinterpret_cast<float*>(p);
+    p += align256((size_t)nq * 4);
+    a.count = reinterpret_cast<uint32_t*>(p);
+    p += align256((size_t)nq * 4);
+    a.cand = reinterpret_cast<uint64_t*>(p);
+    hipError_t e = is::launch_topk(a, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    e = hipEventRecord(sl->done, st);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
   return IS_OK;
 }

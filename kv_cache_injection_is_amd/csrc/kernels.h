@@ -34,19 +34,28 @@ hipError_t launch_inject(const InjectLaunch& a, hipStream_t stream);
 
 struct TopkLaunch {
   const uint16_t* emb;    // [n_facts][emb_dim] fp16
-  const uint16_t* q;      // [n_q][emb_dim] fp16
+  const uint16_t* q;      // [n_q][emb_dim] fp16, n_q <= 128
   int64_t n_facts;
+  int64_t sample_n;       // facts [0, sample_n) give the threshold
   int32_t emb_dim;
   int32_t n_q;
   int32_t k;
-  int32_t n_wg;           // workgroups per query block in stage 1
-  uint64_t* partial;      // [n_q][n_wg][k] packed (score, id) keys
+  int32_t reserved0;
+  float* sample;          // [n_q][sample_n] sample scores (scratch)
+  float* tau;             // [n_q] bound on each query's k-th best score (scratch)
+  uint32_t* count;        // [n_q] candidates found (scratch)
+  uint64_t* cand;         // [n_q][n_facts] candidate (score, id) keys (scratch)
   int32_t* ids;           // [n_q][k]
   float* scores;          // [n_q][k]
 };
 
-// Stage-1 workgroup count for a store of n_facts facts.
-int topk_workgroups(int64_t n_facts);
+// Facts in the threshold sample for a store of n_facts facts.
+int64_t topk_sample_size(int64_t n_facts);
+// Scratch bytes for one call of n_q (<= 128) queries.
+inline size_t topk_scratch_bytes(int64_t n_facts, int32_t n_q) {
+  const size_t s = (size_t)topk_sample_size(n_facts);
+  return (size_t)n_q * (s * 4 + 256) + (size_t)n_q * 8 * 2 + 1024 + (size_t)n_q * n_facts * 8;
+}
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
 
 }  // namespace is

@@ -6,25 +6,28 @@
 // the pages do not describe the index, so this is an exact brute-force
 // search.  Order: score descending, ties to the lower fact id.
 //
-// Stage 1 (persistent, one workgroup of 4 waves per CU, one wave per SIMD):
-// scores = E . Q^T on the matrix cores (v_mfma_f32_32x32x16_f16, fp32
-// accumulation).  A 256-fact tile is split over the 4 waves (64 facts each,
-// two 32-row MFMA tiles) against all 128 queries of a query block.  The A
-// operand (embedding rows) streams from HBM straight into registers one
-// 128-dim chunk ahead; the B operand (queries) comes from a double-buffered
-// LDS copy of the current chunk.  The dot product is order-free in k, so at
-// k-step s lane (row, grp) holds halves [(2s+grp)*8, +8) of the chunk for
-// both operands, which makes the two lanes of a row read 32 contiguous
-// bytes per load.  After each half tile the scores go through LDS to the
-// wave that owns the query (32 queries per wave).  Each query keeps its best
-// 64 (score, id) keys sorted, one per lane, and its k-th best key in a
-// lane register: the first half tile a workgroup sees is sorted outright
-// (bitonic network across the wave); afterwards a ballot against the k-th
-// best rejects most queries at once, and surviving keys are inserted one by
-// one (ballot/popcount and a one-lane shift).  The next tile's first chunk
-// is already in flight during this selection.
-// Stage 2 (one workgroup per query): the sorted per-workgroup lists are
-// staged in LDS and a 64-lane tournament emits the k best heads in order.
+// The selection rests on one fact: the k-th largest score within any subset
+// of the facts is a lower bound on the k-th largest score overall.
+//   1. scan (sample mode): MFMA scores of facts [0, S) (S = a few percent of
+//      the store) for every query, written out;
+//   2. threshold: per query, the exact k-th largest sample score by an
+//      8-bit-digit radix select; that is the bound tau;
+//   3. scan (stream mode): MFMA scores of all facts; a score >= tau is a
+//      candidate, appended to the query's list with one atomic -- about
+//      k*N/S of them, while every true top-k fact is among them;
+//   4. final: per query, radix select of the k-th largest candidate key
+//      (score, then lower id), then the k winners sorted across a wave.
+// The scan (persistent, one workgroup of 4 waves per CU): a 256-fact tile is
+// split over the 4 waves (64 facts each, two 32-row MFMA tiles,
+// v_mfma_f32_32x32x16_f16, fp32 accumulation) against all 128 queries of a
+// query block.  The A operand (embedding rows) streams from HBM straight
+// into registers one 128-dim chunk ahead; the B operand (queries) comes from
+// a double-buffered LDS copy of the current chunk.  The dot product is
+// order-free in k, so at k-step s lane (row, grp) holds halves
+// [(2s+grp)*8, +8) of the chunk for both operands, which makes the two
+// lanes of a row read 32 contiguous bytes per load.  Both scan modes run the
+// same instruction sequence per tile, so a sample fact scores identically
+// in both.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -42,9 +45,6 @@ constexpr int kQB = 128;            // queries per block
 constexpr int kFTW = 64;            // facts per wave per tile (two MFMA row tiles)
 constexpr int kFT = kWaves * kFTW;  // facts per tile
 constexpr int kMaxK = 64;
-constexpr int kHalfRows = kFT / 2;  // score rows staged per epilogue pass
-constexpr int kSPitch = kQB + 1;    // floats per staged score row
-constexpr int kQPW = kQB / kWaves;  // queries owned by a wave in selection
 
 // Order-preserving map of a float to uint32 (larger float -> larger code).
 __device__ __forceinline__ uint32_t ord_of(float s) {
@@ -65,29 +65,13 @@ __device__ __forceinline__ uint64_t key_of(uint32_t ord, uint32_t id) {
 template <int KC>
 struct Smem {
   static constexpr int kQPitch = KC + 8;   // halves per staged query row
-  union {
-    _Float16 q[2][kQB * kQPitch];
-    float s[kHalfRows * kSPitch];
-  } u;
-  uint64_t list[kQB * kMaxK];              // [query][64], sorted descending
+  _Float16 q[2][kQB * kQPitch];
 };
 
 __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   const int lo = __shfl_xor((int)(uint32_t)v, m);
   const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-__device__ __forceinline__ uint64_t shfl_up64(uint64_t v, int d) {
-  const int lo = __shfl_up((int)(uint32_t)v, d);
-  const int hi = __shfl_up((int)(uint32_t)(v >> 32), d);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
 }
 
 // Sorts the wave's 64*P keys descending; key r of lane l is element r*64+l.
@@ -127,30 +111,8 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t (&a)[P]) {
   }
 }
 
-// Inserts x into the descending 64-entry list held one entry per lane.
-__device__ __forceinline__ void wave_insert(uint64_t& L, uint64_t x) {
-  const int lane = threadIdx.x & 63;
-  const int pos = __popcll(__ballot(L > x));
-  const uint64_t up = shfl_up64(L, 1);
-  L = lane < pos ? L : (lane == pos ? x : up);
-}
-
-// Inserts the keys of `m` (lanes of `key`) that beat the k-th best into L.
-__device__ __forceinline__ void insert_masked(uint64_t& L, uint64_t& tau, uint64_t key,
-                                              uint64_t m, int k) {
-  while (m) {
-    const int i = __builtin_ctzll(m);
-    m &= m - 1;
-    const uint64_t x = readlane64(key, i);
-    if (x > tau) {
-      wave_insert(L, x);
-      tau = readlane64(L, k - 1);
-    }
-  }
-}
-
-template <int KC>
-__global__ __launch_bounds__(kThreads) void topk_stage1(TopkLaunch a) {
+template <int KC, bool kSample>
+__global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
   constexpr int kQPitch = Smem<KC>::kQPitch;
   constexpr int kLoads = KC / 16;            // 16-byte loads per lane per chunk and row tile
   constexpr int kSteps = KC / 16;            // MFMA k-steps per chunk
@@ -164,10 +126,18 @@ __global__ __launch_bounds__(kThreads) void topk_stage1(TopkLaunch a) {
   const int qb0 = blockIdx.y * kQB;
   const int D = a.emb_dim;
   const int n_chunks = D / KC;
-  const int k = a.k;
-  const int64_t n_tiles = (a.n_facts + kFT - 1) / kFT;
+  const int64_t limit = kSample ? a.sample_n : a.n_facts;
+  const int64_t n_tiles = (limit + kFT - 1) / kFT;
   int64_t tile = blockIdx.x;
   if (tile >= n_tiles) return;
+
+  // Threshold of this lane's query in each 32-query tile.
+  float tau[4];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    const int q = qb0 + qt * 32 + row;
+    tau[qt] = (!kSample && q < a.n_q) ? a.tau[q] : 0.f;
+  }
 
   // Query chunk staging: 16-byte pieces loaded to registers before the
   // embedding loads of the same chunk (so waiting for them leaves the
@@ -192,11 +162,11 @@ __global__ __launch_bounds__(kThreads) void topk_stage1(TopkLaunch a) {
     for (int i = 0; i < kQPer; ++i) {
       const int p = tid + i * kThreads;
       const int qr = p / (KC / 8), col = (p % (KC / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&sm.u.q[b][qr * kQPitch + col]) = qreg[i];
+      *reinterpret_cast<u32x4*>(&sm.q[b][qr * kQPitch + col]) = qreg[i];
     }
   };
   // This lane's embedding rows in tile t (rows past the end are clamped to
-  // the last row and masked in the epilogue).
+  // the last row and masked when scores are emitted).
   const uint16_t* erow[2];
   auto set_rows = [&](int64_t t, const uint16_t* (&dst)[2]) {
 #pragma unroll
@@ -218,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void topk_stage1(TopkLaunch a) {
   // MFMAs of one chunk; the query fragments of k-step s+1 are read from LDS
   // while the eight MFMAs of step s run.
   auto compute = [&](const u32x4 (&eb)[2][kLoads], int b) {
-    const _Float16* qs = sm.u.q[b] + row * kQPitch + grp * 8;
+    const _Float16* qs = sm.q[b] + row * kQPitch + grp * 8;
     half8 bq[4], bn[4];
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt)
@@ -241,22 +211,6 @@ __global__ __launch_bounds__(kThreads) void topk_stage1(TopkLaunch a) {
       for (int qt = 0; qt < 4; ++qt) bq[qt] = bn[qt];
     }
   };
-
-  // Selection state: lane j < kQPW of this wave holds the k-th best key of
-  // its query j (0 until the lists exist).
-  uint64_t tau_reg = 0;
-  bool have_lists = false;
-
-  // One stream of chunks over this workgroup's tiles: the loads of the
-  // next chunk -- the next tile's first chunk at a tile's end -- go to e1
-  // before the MFMAs of the current chunk (in e0), and stay in flight
-  // through the selection at a tile's end; e1 moves to e0 when the MFMAs
-  // need it.  Query chunk c sits in LDS buffer c & 1.
-  set_rows(tile, erow);
-  load_q(0);
-  load_e(e0, erow, 0);
-  store_q(0);
-  __syncthreads();
   auto zero_acc = [&] {
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
@@ -265,6 +219,53 @@ __global__ __launch_bounds__(kThreads) void topk_stage1(TopkLaunch a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[ft][qt][e] = 0.f;
   };
+  // Scores of tile t out: every score (sample mode) or those >= tau.
+  // Accumulator element e of lane (row, grp) is fact row 8*(e/4) + 4*grp +
+  // e%4 of its 32-row tile and query column `row` of its 32-query tile.
+  auto emit = [&](int64_t t) {
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+      const int64_t fbase = t * kFT + wave * kFTW + ft * 32 + 4 * grp;
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const int q = qb0 + qt * 32 + row;
+        if (q >= a.n_q) continue;
+        if (kSample) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t f = fbase + 8 * (e / 4) + (e % 4);
+            if (f < limit) a.sample[(int64_t)q * a.sample_n + f] = acc[ft][qt][e];
+          }
+        } else {
+          uint32_t m = 0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t f = fbase + 8 * (e / 4) + (e % 4);
+            m |= (f < limit && acc[ft][qt][e] >= tau[qt]) ? (1u << e) : 0u;
+          }
+          if (m) {   // rare: one counter bump per lane and row tile
+            uint32_t pos = atomicAdd(&a.count[q], (uint32_t)__builtin_popcount(m));
+            uint64_t* dst = a.cand + (int64_t)q * a.n_facts;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (m & (1u << e))
+                dst[pos++] = key_of(ord_of(acc[ft][qt][e]),
+                                    (uint32_t)(fbase + 8 * (e / 4) + (e % 4)));
+          }
+        }
+      }
+    }
+  };
+
+  // One stream of chunks over this workgroup's tiles: the loads of the
+  // next chunk -- the next tile's first chunk at a tile's end -- go to e1
+  // before the MFMAs of the current chunk (in e0); e1 moves to e0 when the
+  // MFMAs need it.  Query chunk c sits in LDS buffer c & 1.
+  set_rows(tile, erow);
+  load_q(0);
+  load_e(e0, erow, 0);
+  store_q(0);
+  __syncthreads();
   zero_acc();
   int c = 0;
   while (true) {
@@ -275,149 +276,111 @@ __global__ __launch_bounds__(kThreads) void topk_stage1(TopkLaunch a) {
     if (last && has_next) set_rows(next_tile, nrow);
     const int next_c = last ? 0 : c + 1;
     if (has_next) {
-      if (!last) load_q(next_c);
+      load_q(next_c);
       load_e(e1, nrow, next_c);
     }
     compute(e0, c & 1);
-    if (!last) {
-      store_q(next_c & 1);
-#pragma unroll
-      for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) e0[ft][i] = e1[ft][i];
-      __syncthreads();
-      c = next_c;
-      continue;
+    if (last) {
+      emit(tile);
+      zero_acc();
+      if (!has_next) break;
+      tile = next_tile;
+      erow[0] = nrow[0];
+      erow[1] = nrow[1];
     }
-    __syncthreads();   // the staged scores below reuse the query buffers
-
-    // Selection: two passes of 128 fact rows through LDS to the query-owning waves.
-    const int64_t fact0 = tile * kFT;
-    for (int pass = 0; pass < 2; ++pass) {
-      const int64_t f0 = fact0 + pass * kHalfRows;
-      if (f0 >= a.n_facts) break;                       // uniform
-      const int valid = (int)min<int64_t>(kHalfRows, a.n_facts - f0);
-      if (wave / 2 == pass) {
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft) {
-          const int rbase = (wave % 2) * kFTW + ft * 32;
-#pragma unroll
-          for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int fr = rbase + 8 * (e / 4) + 4 * grp + (e % 4);
-              sm.u.s[fr * kSPitch + qt * 32 + row] = acc[ft][qt][e];
-            }
-        }
-      }
-      __syncthreads();
-      const int q0 = wave * kQPW;
-      const int nq = min(kQPW, a.n_q - qb0 - q0);       // uniform per wave
-      // all of this wave's staged scores at once: one LDS round trip
-      float s0[kQPW], s1[kQPW];
-#pragma unroll
-      for (int j = 0; j < kQPW; ++j) {
-        s0[j] = sm.u.s[lane * kSPitch + q0 + j];
-        s1[j] = sm.u.s[(64 + lane) * kSPitch + q0 + j];
-      }
-      const bool ok0 = lane < valid, ok1 = 64 + lane < valid;
-      const uint32_t id0 = (uint32_t)(f0 + lane), id1 = (uint32_t)(f0 + 64 + lane);
-#pragma unroll
-      for (int j = 0; j < kQPW; ++j) {
-        if (j >= nq) break;
-        const uint64_t key0 = ok0 ? key_of(ord_of(s0[j]), id0) : 0;
-        const uint64_t key1 = ok1 ? key_of(ord_of(s1[j]), id1) : 0;
-        const int q = q0 + j;
-        uint64_t L;
-        if (!have_lists) {
-          uint64_t v[2] = {key0, key1};
-          wave_sort_desc<2>(v);
-          L = v[0];
-        } else {
-          uint64_t tau = readlane64(tau_reg, j);
-          const uint64_t m0 = __ballot(key0 > tau);
-          const uint64_t m1 = __ballot(key1 > tau);
-          if ((m0 | m1) == 0) continue;
-          L = sm.list[q * kMaxK + lane];
-          insert_masked(L, tau, key0, m0, k);
-          insert_masked(L, tau, key1, m1, k);
-        }
-        sm.list[q * kMaxK + lane] = L;
-        const uint64_t t = readlane64(L, k - 1);
-        if (lane == j) tau_reg = t;
-      }
-      have_lists = true;
-      __syncthreads();
-    }
-    if (!has_next) break;
-    load_q(0);
-    store_q(0);
+    __syncthreads();   // every wave is done with query buffer next_c & 1
+    store_q(next_c & 1);
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) e0[ft][i] = e1[ft][i];
     __syncthreads();
-    tile = next_tile;
-    erow[0] = nrow[0];
-    erow[1] = nrow[1];
-    c = 0;
-    zero_acc();
-  }
-
-  // Write each query's sorted list (the first k entries).
-  for (int j = 0; j < kQPW; ++j) {
-    const int q = wave * kQPW + j;
-    if (qb0 + q >= a.n_q) break;
-    if (lane < k)
-      a.partial[((int64_t)(qb0 + q) * a.n_wg + blockIdx.x) * k + lane] = sm.list[q * kMaxK + lane];
+    c = next_c;
   }
 }
 
-constexpr int kMergeThreads = 256;
+constexpr int kSelThreads = 256;
 
-// Stage 2: the k best of n_wg sorted lists of k keys, by a tournament over
-// the list heads held by the 64 lanes of wave 0 (lane l owns lists l,
-// l+64, l+128, l+192).
-__global__ __launch_bounds__(kMergeThreads) void topk_stage2(TopkLaunch a) {
-  __shared__ uint64_t buf[256 * kMaxK];
-  const int q = blockIdx.x;
-  const int k = a.k;
-  const int n = a.n_wg;
-  const uint64_t* src = a.partial + (int64_t)q * n * k;
-  for (int i = threadIdx.x; i < n * k; i += kMergeThreads) buf[i] = src[i];
-  __syncthreads();
-  if (threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
-  int ptr[4];
-  uint64_t head[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int list = lane + 64 * m;
-    ptr[m] = 0;
-    head[m] = list < n ? buf[list * k] : 0;
-  }
-  for (int s = 0; s < k; ++s) {
-    uint64_t best = head[0];
-#pragma unroll
-    for (int m = 1; m < 4; ++m) best = head[m] > best ? head[m] : best;
-    uint64_t g = best;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint64_t o = shfl_xor64(g, off);
-      g = o > g ? o : g;
+// The k-th largest of n values (32- or 64-bit) in global memory, by
+// most-significant-digit radix select over 8-bit digits.  All threads of
+// the workgroup call it; the result is returned to all.
+template <typename V>
+__device__ V radix_kth_largest(const V* vals, int64_t n, int k, uint32_t* hist, V* share) {
+  constexpr int kBits = 8 * sizeof(V);
+  V prefix = 0, mask = 0;
+  int remaining = k;
+  for (int shift = kBits - 8; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += kSelThreads) {
+      const V v = vals[i];
+      if ((v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & 255u], 1u);
     }
-    // real keys are distinct, so exactly one head equals g
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (head[m] == g) {
-        const int list = lane + 64 * m;
-        ++ptr[m];
-        head[m] = ptr[m] < k ? buf[list * k + ptr[m]] : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t above = 0;
+      int b = 255;
+      for (; b > 0; --b) {
+        if (above + hist[b] >= (uint32_t)remaining) break;
+        above += hist[b];
       }
+      share[0] = (V)b;
+      share[1] = (V)above;
     }
-    if (lane == 0) {
-      a.ids[(int64_t)q * k + s] = (int32_t)(0xFFFFFFFFu - (uint32_t)g);
-      a.scores[(int64_t)q * k + s] = float_of((uint32_t)(g >> 32));
+    __syncthreads();
+    const V b = share[0];
+    remaining -= (int)share[1];
+    prefix |= b << shift;
+    mask |= (V)255 << shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// Per query: the bound tau = k-th largest sample score (lowered by a hair
+// so that a fact scoring exactly tau in the sample still passes), and the
+// candidate counter cleared for the stream scan.
+__global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t share[2];
+  const int q = blockIdx.x;
+  const float* v = a.sample + (int64_t)q * a.sample_n;
+  // float order as uint32 order: compare the order-preserving codes
+  uint32_t* codes = reinterpret_cast<uint32_t*>(a.sample) + (int64_t)q * a.sample_n;
+  for (int64_t i = threadIdx.x; i < a.sample_n; i += kSelThreads) codes[i] = ord_of(v[i]);
+  __syncthreads();
+  const uint32_t kth = radix_kth_largest<uint32_t>(codes, a.sample_n, a.k, hist, share);
+  if (threadIdx.x == 0) {
+    const float t = float_of(kth);
+    a.tau[q] = t - (fabsf(t) * 0x1p-20f + 0x1p-100f);
+    a.count[q] = 0;
+  }
+}
+
+// Per query: the k best candidates, in order.
+__global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t share[2];
+  __shared__ uint64_t best[kMaxK];
+  __shared__ uint32_t n_best;
+  const int q = blockIdx.x;
+  const int64_t n = a.count[q];
+  const uint64_t* keys = a.cand + (int64_t)q * a.n_facts;
+  const uint64_t kth = radix_kth_largest<uint64_t>(keys, n, a.k, hist, share);
+  if (threadIdx.x == 0) n_best = 0;
+  if (threadIdx.x < kMaxK) best[threadIdx.x] = 0;
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < n; i += kSelThreads) {
+    const uint64_t v = keys[i];
+    if (v >= kth) best[atomicAdd(&n_best, 1u)] = v;   // exactly k keys (keys are distinct)
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    uint64_t v[1] = {best[threadIdx.x]};
+    wave_sort_desc<1>(v);
+    if (threadIdx.x < a.k) {
+      a.ids[(int64_t)q * a.k + threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[0]);
+      a.scores[(int64_t)q * a.k + threadIdx.x] = float_of((uint32_t)(v[0] >> 32));
     }
   }
 }
@@ -429,19 +392,32 @@ int topk_workgroups(int64_t n_facts) {
   return (int)(tiles < 256 ? tiles : 256);
 }
 
+int64_t topk_sample_size(int64_t n_facts) {
+  int64_t s = n_facts / 32;
+  if (s < 4096) s = 4096;
+  s = (s + kFT - 1) / kFT * kFT;
+  return s < n_facts ? s : n_facts;
+}
+
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
   if (a.n_q == 0) return hipSuccess;
-  if (a.k < 1 || a.k > kMaxK || a.n_wg < 1 || a.n_wg > 256) return hipErrorInvalidValue;
-  const dim3 grid1((unsigned)a.n_wg, (unsigned)((a.n_q + kQB - 1) / kQB));
-  if (a.emb_dim % 128 == 0)
-    hipLaunchKernelGGL(topk_stage1<128>, grid1, dim3(kThreads), 0, stream, a);
-  else if (a.emb_dim % 32 == 0)
-    hipLaunchKernelGGL(topk_stage1<32>, grid1, dim3(kThreads), 0, stream, a);
-  else
+  if (a.k < 1 || a.k > kMaxK || a.k > a.sample_n || a.n_q > kQB) return hipErrorInvalidValue;
+  const unsigned qblocks = (unsigned)((a.n_q + kQB - 1) / kQB);
+  const dim3 g_sample((unsigned)topk_workgroups(a.sample_n), qblocks);
+  const dim3 g_stream((unsigned)topk_workgroups(a.n_facts), qblocks);
+  if (a.emb_dim % 128 == 0) {
+    hipLaunchKernelGGL((topk_scan<128, true>), g_sample, dim3(kThreads), 0, stream, a);
+  } else if (a.emb_dim % 32 == 0) {
+    hipLaunchKernelGGL((topk_scan<32, true>), g_sample, dim3(kThreads), 0, stream, a);
+  } else {
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_stage2, dim3((unsigned)a.n_q), dim3(kMergeThreads), 0, stream, a);
+  }
+  hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
+  if (a.emb_dim % 128 == 0)
+    hipLaunchKernelGGL((topk_scan<128, false>), g_stream, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((topk_scan<32, false>), g_stream, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(topk_final, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 
