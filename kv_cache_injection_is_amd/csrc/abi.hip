@@ -50,6 +50,16 @@ constexpr int kSlots = 4;
 
 }  // namespace
 
+// A pinned, device-mapped piece of the host tier holding whole facts
+// [f0, f1) back to back.
+struct HostChunk {
+  void* k = nullptr;
+  void* v = nullptr;
+  int64_t f0 = 0, f1 = 0;
+};
+
+constexpr size_t kHostChunkBytes = size_t(4) << 30;
+
 struct is_store {
   int device = 0;
   int32_t L = 0, H = 0, d = 0, dtype = 0, emb_dim = 0;
@@ -57,12 +67,11 @@ struct is_store {
   std::vector<int32_t> len;
   std::vector<int64_t> tok_off;   // [n_facts + 1]
   size_t es = 0;
-  void* k_dev = nullptr;
+  void* k_dev = nullptr;          // HBM arenas, facts [0, n_hbm)
   void* v_dev = nullptr;
-  void* k_host = nullptr;         // pinned, mapped
-  void* v_host = nullptr;
-  void* k_host_dev = nullptr;     // device aliases of the pinned arenas
-  void* v_host_dev = nullptr;
+  std::vector<HostChunk> host;    // pinned tier, facts [n_hbm, n_facts)
+  std::vector<uint64_t> k_addr;   // [n_facts] device-visible block addresses
+  std::vector<uint64_t> v_addr;
   uint16_t* emb = nullptr;
   std::mutex mu;
   Slot slots[kSlots];
@@ -72,12 +81,25 @@ struct is_store {
   size_t fact_bytes(int64_t f0, int64_t f1) const {
     return (size_t)(tok_off[f1] - tok_off[f0]) * row_elems() * es;
   }
-  // Address of fact f's block in its arena (host pointer for host facts).
+  // Host-side address of fact f's K or V block (for host-tier facts, the
+  // pinned host pointer).
+  const HostChunk& chunk_of(int64_t f) const {
+    size_t lo = 0, hi = host.size() - 1;
+    while (lo < hi) {
+      const size_t mid = (lo + hi + 1) / 2;
+      if (host[mid].f0 <= f) lo = mid; else hi = mid - 1;
+    }
+    return host[lo];
+  }
   char* k_at(int64_t f) const {
-    return f < n_hbm ? (char*)k_dev + fact_bytes(0, f) : (char*)k_host + fact_bytes(n_hbm, f);
+    if (f < n_hbm) return (char*)k_dev + fact_bytes(0, f);
+    const HostChunk& c = chunk_of(f);
+    return (char*)c.k + fact_bytes(c.f0, f);
   }
   char* v_at(int64_t f) const {
-    return f < n_hbm ? (char*)v_dev + fact_bytes(0, f) : (char*)v_host + fact_bytes(n_hbm, f);
+    if (f < n_hbm) return (char*)v_dev + fact_bytes(0, f);
+    const HostChunk& c = chunk_of(f);
+    return (char*)c.v + fact_bytes(c.f0, f);
   }
 };
 
@@ -94,8 +116,10 @@ void free_store(is_store* s) {
   }
   if (s->k_dev) (void)hipFree(s->k_dev);
   if (s->v_dev) (void)hipFree(s->v_dev);
-  if (s->k_host) (void)hipHostFree(s->k_host);
-  if (s->v_host) (void)hipHostFree(s->v_host);
+  for (HostChunk& c : s->host) {
+    if (c.k) (void)hipHostFree(c.k);
+    if (c.v) (void)hipHostFree(c.v);
+  }
   if (s->emb) (void)hipFree(s->emb);
   delete s;
 }
@@ -140,7 +164,8 @@ is::StoreGeom geom_of(const is_store* s) {
   g.dtype = s->dtype;
   g.n_facts = s->n_facts;
   g.fact_len = s->len.data();
-  g.tok_off = s->tok_off.data();
+  g.k_addr = s->k_addr.data();
+  g.v_addr = s->v_addr.data();
   g.n_hbm = s->n_hbm;
   return g;
 }
@@ -179,22 +204,46 @@ IS_EXPORT int is_store_create(const is_store_desc* d, is_store** out) {
                s->tok_off.begin() - 1;
   }
   const size_t hbm_bytes = s->fact_bytes(0, s->n_hbm);
-  const size_t host_bytes = s->fact_bytes(s->n_hbm, s->n_facts);
   if (hbm_bytes > 0 && (hipMalloc(&s->k_dev, hbm_bytes) != hipSuccess ||
                         hipMalloc(&s->v_dev, hbm_bytes) != hipSuccess)) {
     free_store(s);
     return fail(IS_ERR_OOM, "device allocation of the fact store failed");
   }
-  if (host_bytes > 0) {
-    if (hipHostMalloc(&s->k_host, host_bytes, hipHostMallocMapped) != hipSuccess ||
-        hipHostMalloc(&s->v_host, host_bytes, hipHostMallocMapped) != hipSuccess) {
+  // Host tier: pinned chunks of at most 4 GiB (a longer fact gets its own).
+  for (int64_t f0 = s->n_hbm; f0 < s->n_facts;) {
+    int64_t f1 = f0 + 1;
+    while (f1 < s->n_facts && s->fact_bytes(f0, f1 + 1) <= kHostChunkBytes) ++f1;
+    HostChunk c;
+    c.f0 = f0;
+    c.f1 = f1;
+    const size_t bytes = s->fact_bytes(f0, f1);
+    const bool ok = hipHostMalloc(&c.k, bytes, hipHostMallocMapped) == hipSuccess &&
+                    hipHostMalloc(&c.v, bytes, hipHostMallocMapped) == hipSuccess;
+    s->host.push_back(c);
+    if (!ok) {
       free_store(s);
       return fail(IS_ERR_OOM, "pinned host allocation of the fact store failed");
     }
-    if (hipHostGetDevicePointer(&s->k_host_dev, s->k_host, 0) != hipSuccess ||
-        hipHostGetDevicePointer(&s->v_host_dev, s->v_host, 0) != hipSuccess) {
+    f0 = f1;
+  }
+  // Device-visible block address of every fact.
+  s->k_addr.resize((size_t)s->n_facts);
+  s->v_addr.resize((size_t)s->n_facts);
+  for (int64_t f = 0; f < s->n_hbm; ++f) {
+    s->k_addr[f] = (uint64_t)(uintptr_t)((char*)s->k_dev + s->fact_bytes(0, f));
+    s->v_addr[f] = (uint64_t)(uintptr_t)((char*)s->v_dev + s->fact_bytes(0, f));
+  }
+  for (const HostChunk& c : s->host) {
+    void* kd = nullptr;
+    void* vd = nullptr;
+    if (hipHostGetDevicePointer(&kd, c.k, 0) != hipSuccess ||
+        hipHostGetDevicePointer(&vd, c.v, 0) != hipSuccess) {
       free_store(s);
       return fail(IS_ERR_HIP, "hipHostGetDevicePointer failed");
+    }
+    for (int64_t f = c.f0; f < c.f1; ++f) {
+      s->k_addr[f] = (uint64_t)(uintptr_t)((char*)kd + s->fact_bytes(c.f0, f));
+      s->v_addr[f] = (uint64_t)(uintptr_t)((char*)vd + s->fact_bytes(c.f0, f));
     }
   }
   if (s->emb_dim > 0 &&
@@ -234,14 +283,19 @@ IS_EXPORT int is_store_load(is_store* s, int64_t first, int64_t n, const void* k
   size_t src_off = 0;
   for (const Part& p : parts) {
     if (p.f1 <= p.f0) continue;
-    const size_t bytes = s->fact_bytes(p.f0, p.f1);
     const hipMemcpyKind kind = p.host ? from_dev_to_host : from_dev;
-    hipError_t e;
-    if (k && (e = hipMemcpy(s->k_at(p.f0), (const char*)k + src_off, bytes, kind)) != hipSuccess)
-      return hip_fail(e, "K load");
-    if (v && (e = hipMemcpy(s->v_at(p.f0), (const char*)v + src_off, bytes, kind)) != hipSuccess)
-      return hip_fail(e, "V load");
-    src_off += bytes;
+    // HBM facts are one span; host facts are copied chunk by chunk.
+    for (int64_t f = p.f0; f < p.f1;) {
+      const int64_t g = p.host ? std::min(p.f1, s->chunk_of(f).f1) : p.f1;
+      const size_t bytes = s->fact_bytes(f, g);
+      hipError_t e;
+      if (k && (e = hipMemcpy(s->k_at(f), (const char*)k + src_off, bytes, kind)) != hipSuccess)
+        return hip_fail(e, "K load");
+      if (v && (e = hipMemcpy(s->v_at(f), (const char*)v + src_off, bytes, kind)) != hipSuccess)
+        return hip_fail(e, "V load");
+      src_off += bytes;
+      f = g;
+    }
   }
   if (emb) {
     hipError_t e = hipMemcpy(s->emb + first * s->emb_dim, emb, (size_t)n * s->emb_dim * 2, from_dev);
@@ -307,7 +361,7 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
 #if IS_SORT_WORK
   // Launch order only: workgroups then sweep the store in address order.
   std::sort(items.begin(), items.end(), [](const is::WorkItem& x, const is::WorkItem& y) {
-    return x.tier != y.tier ? x.tier < y.tier : x.elem_off < y.elem_off;
+    return x.tier != y.tier ? x.tier < y.tier : x.k < y.k;
   });
 #endif
   is::plan_rope(s->d, rope, &g);
@@ -329,10 +383,6 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
   if (e != hipSuccess) return hip_fail(e, "staging copy");
   is::InjectLaunch a{};
   char* dv = static_cast<char*>(sl->dev);
-  a.k_dev = s->k_dev;
-  a.v_dev = s->v_dev;
-  a.k_host = s->k_host_dev;
-  a.v_host = s->v_host_dev;
   a.kc = cache->k_base;
   a.vc = cache->v_base;
   a.s_layer = cache->stride_layer;

@@ -7,6 +7,9 @@
 // values, are scatter-copied into the paged KV cache.  Rotation reading:
 // rotate-half pairs (i, i + d/2) turn by p * f_i.
 //
+// Facts of the pinned host tier are read by the same code through their
+// device-visible addresses (zero-copy over PCIe).
+//
 // Design (gfx950): one workgroup of 256 lanes per (selected fact, layer).
 // The fact's [kv_head][token][head_dim] block for that layer is contiguous
 // in the store, so the workgroup streams it with 16-byte loads.  A lane owns
@@ -175,11 +178,9 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectLaunch a) {
   const WorkItem w = a.work[blockIdx.x];
   const int layer = blockIdx.y;
   const int len = w.len;
-  const int64_t layer_off = (w.elem_off + (int64_t)layer * a.n_heads * len * D) * ES;
-  const char* __restrict__ ksrc =
-      static_cast<const char*>(w.tier ? a.k_host : a.k_dev) + layer_off;
-  const char* __restrict__ vsrc =
-      static_cast<const char*>(w.tier ? a.v_host : a.v_dev) + layer_off;
+  const int64_t layer_off = (int64_t)layer * a.n_heads * len * D * ES;
+  const char* __restrict__ ksrc = reinterpret_cast<const char*>(w.k) + layer_off;
+  const char* __restrict__ vsrc = reinterpret_cast<const char*>(w.v) + layer_off;
   char* __restrict__ kc = static_cast<char*>(a.kc);
   char* __restrict__ vc = static_cast<char*>(a.vc);
   const int32_t* __restrict__ bt = a.bt + (int64_t)w.req * a.max_blocks;
@@ -273,9 +274,9 @@ __global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
   const int nl = min(G, a.n_layers - l0);
   const int len = w.len;
   const int H = a.n_heads;
-  const int64_t base = (w.elem_off + (int64_t)l0 * H * len * D) * ES;
-  const char* __restrict__ ksrc = static_cast<const char*>(w.tier ? a.k_host : a.k_dev) + base;
-  const char* __restrict__ vsrc = static_cast<const char*>(w.tier ? a.v_host : a.v_dev) + base;
+  const int64_t base = (int64_t)l0 * H * len * D * ES;
+  const char* __restrict__ ksrc = reinterpret_cast<const char*>(w.k) + base;
+  const char* __restrict__ vsrc = reinterpret_cast<const char*>(w.v) + base;
   char* __restrict__ kc = static_cast<char*>(a.kc);
   char* __restrict__ vc = static_cast<char*>(a.vc);
   const int32_t* __restrict__ bt = a.bt + (int64_t)w.req * a.max_blocks;

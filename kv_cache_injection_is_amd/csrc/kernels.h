@@ -10,10 +10,6 @@
 namespace is {
 
 struct InjectLaunch {
-  const void* k_dev;      // HBM arenas
-  const void* v_dev;
-  const void* k_host;     // device-visible aliases of the pinned host arenas
-  const void* v_host;
   void* kc;               // cache bases
   void* vc;
   int64_t s_layer, s_block, s_slot, s_head;   // cache strides (elements)

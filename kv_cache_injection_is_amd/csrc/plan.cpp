@@ -163,7 +163,6 @@ int plan_inject(const StoreGeom& g, int32_t n_req, const int32_t* req_off,
                                       std::to_string(j) + " is outside [0, n_facts)");
 
   const int64_t B = c->block_size;
-  const int64_t row = (int64_t)g.n_layers * g.n_kv_heads * g.head_dim;
   std::vector<SlotRun> runs;
   int64_t total = 0;
   if (items) {
@@ -178,13 +177,9 @@ int plan_inject(const StoreGeom& g, int32_t n_req, const int32_t* req_off,
       const int64_t len = g.fact_len[f];
       if (pos + len > (int64_t)1 << 24)
         return fail(IS_ERR_INVALID_ARG, "serving positions must stay below 2^24");
-      if (items) {
-        const int64_t tok = g.tok_off ? g.tok_off[f] : 0;
-        const bool host = f >= g.n_hbm;
-        const int64_t base = host ? g.tok_off[g.n_hbm] : 0;
-        items->push_back(WorkItem{(tok - base) * row, (int32_t)len, (int32_t)pos, r,
-                                  host ? 1 : 0});
-      }
+      if (items)
+        items->push_back(WorkItem{g.k_addr[f], g.v_addr[f], (int32_t)len, (int32_t)pos, r,
+                                  f >= g.n_hbm ? 1 : 0});
       pos += len;
     }
     const int64_t first = prefix_len[r], end = pos;   // segment [first, end)

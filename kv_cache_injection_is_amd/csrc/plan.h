@@ -15,24 +15,26 @@ namespace is {
 int fail(int code, const std::string& msg);
 void clear_error();
 
-// One (request, fact) pair of an inject call: where the fact's K/V block
-// starts in its arena (elements), its token count, the serving position of
-// its first token, its request, and its tier (0 = HBM, 1 = pinned host).
+// One (request, fact) pair of an inject call: device-visible addresses of
+// the fact's K and V blocks, its token count, the serving position of its
+// first token, its request, and its tier (0 = HBM, 1 = pinned host).
 struct WorkItem {
-  int64_t elem_off;
+  uint64_t k;
+  uint64_t v;
   int32_t len;
   int32_t pos;
   int32_t req;
   int32_t tier;
 };
-static_assert(sizeof(WorkItem) == 24, "WorkItem layout is shared with the kernel");
+static_assert(sizeof(WorkItem) == 32, "WorkItem layout is shared with the kernel");
 
 // Geometry the planner needs from a store (or a store description).
 struct StoreGeom {
   int32_t n_layers = 0, n_kv_heads = 0, head_dim = 0, dtype = 0;
   int64_t n_facts = 0;
   const int32_t* fact_len = nullptr;   // [n_facts]
-  const int64_t* tok_off = nullptr;    // [n_facts + 1] token offsets, or null
+  const uint64_t* k_addr = nullptr;    // [n_facts] device-visible K block address, or null
+  const uint64_t* v_addr = nullptr;    // [n_facts] device-visible V block address, or null
   int64_t n_hbm = 0;                   // facts [0, n_hbm) in HBM
 };
 

@@ -370,3 +370,29 @@ def smoke() -> None:
             f"max |err| {err:.2e})")
     finally:
         st.destroy()
+
+
+def check_untouched(cache: Cache, written_slots: np.ndarray) -> None:
+    """Every cache row (layer, slot) that no injected token maps to must
+    still hold its sentinel, bit for bit: checked on the whole cache by the
+    generator's device check against a row mask built from the oracle's
+    slot list.  NHD layout only (a slot's heads form one row)."""
+    torch = torch_mod()
+    assert cache.layout == "NHD"
+    w = cache.w
+    n_rows_layer = cache.n_blocks * w.block_size
+    mask = torch.zeros((w.n_layers, n_rows_layer), dtype=torch.uint8, device="cuda")
+    if len(written_slots):
+        idx = torch.as_tensor(np.asarray(written_slots, dtype=np.int64), device="cuda")
+        mask[:, idx] = 1
+    row_bytes = w.n_kv_heads * w.head_dim * w.elem_size
+    bad = torch.zeros(2, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    n = cache.k.numel()
+    synth.gpu_sentinel_check(SENTINEL_SEED_K, cache.k.data_ptr(), n, row_bytes, mask.data_ptr(),
+                             bad.data_ptr(), st)
+    synth.gpu_sentinel_check(SENTINEL_SEED_V, cache.v.data_ptr(), n, row_bytes, mask.data_ptr(),
+                             bad.data_ptr() + 8, st)
+    torch.cuda.synchronize()
+    k_bad, v_bad = (int(x) for x in bad.cpu())
+    assert k_bad == 0 and v_bad == 0, f"untouched rows changed: {k_bad} K words, {v_bad} V words"

@@ -79,7 +79,8 @@ def test_inject_fp32_head128_and_repeat(gpu):
 def test_inject_other_head_dims(gpu, dtype, head_dim):
     """Shapes served by the general kernel (rows other than 256 bytes)."""
     w = SMALL_LLAMA.scaled(name=f"hd{head_dim}", n_layers=3, n_kv_heads=4, head_dim=head_dim,
-                           dtype=dtype, n_facts=50, n_blocks=96, theta=1e4, scaling="none")
+                           dtype=dtype, n_facts=50, n_blocks=400, theta=1e4, scaling="none",
+                           prefix=(0, 40))
     lens, req_off, flat, prefix, bt = _zipf_problem(w, 5, 6)
     st = Hn.make_store(w, lens)
     try:
