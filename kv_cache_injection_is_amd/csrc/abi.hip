@@ -78,6 +78,10 @@ struct is_store {
   int next_slot = 0;
 
   int64_t row_elems() const { return (int64_t)L * H * d; }
+  // Rows allocated for the embeddings (padded to whole tiles when blocked).
+  int64_t emb_rows() const {
+    return is::topk_blocked_layout(emb_dim) ? is::topk_padded_facts(n_facts) : n_facts;
+  }
   size_t fact_bytes(int64_t f0, int64_t f1) const {
     return (size_t)(tok_off[f1] - tok_off[f0]) * row_elems() * es;
   }
@@ -246,10 +250,16 @@ IS_EXPORT int is_store_create(const is_store_desc* d, is_store** out) {
       s->v_addr[f] = (uint64_t)(uintptr_t)((char*)vd + s->fact_bytes(c.f0, f));
     }
   }
-  if (s->emb_dim > 0 &&
-      hipMalloc((void**)&s->emb, (size_t)s->n_facts * s->emb_dim * 2) != hipSuccess) {
-    free_store(s);
-    return fail(IS_ERR_OOM, "device allocation of the embeddings failed");
+  if (s->emb_dim > 0) {
+    const size_t bytes = (size_t)s->emb_rows() * s->emb_dim * 2;
+    if (hipMalloc((void**)&s->emb, bytes) != hipSuccess) {
+      free_store(s);
+      return fail(IS_ERR_OOM, "device allocation of the embeddings failed");
+    }
+    if (hipMemset(s->emb, 0, bytes) != hipSuccess) {
+      free_store(s);
+      return fail(IS_ERR_HIP, "hipMemset of the embeddings failed");
+    }
   }
   if (d->k_src || d->v_src || d->emb_src) {
     rc = is_store_load(s, 0, s->n_facts, d->k_src, d->v_src, d->emb_src, 0);
@@ -297,8 +307,23 @@ IS_EXPORT int is_store_load(is_store* s, int64_t first, int64_t n, const void* k
       f = g;
     }
   }
-  if (emb) {
+  if (emb && !is::topk_blocked_layout(s->emb_dim)) {
     hipError_t e = hipMemcpy(s->emb + first * s->emb_dim, emb, (size_t)n * s->emb_dim * 2, from_dev);
+    if (e != hipSuccess) return hip_fail(e, "embedding load");
+  } else if (emb) {
+    // rows to device memory in pieces, then scattered into the blocked layout
+    const int64_t piece_rows = 65536;
+    uint16_t* tmp = nullptr;
+    const size_t tmp_bytes = (size_t)std::min<int64_t>(n, piece_rows) * s->emb_dim * 2;
+    if (hipMalloc((void**)&tmp, tmp_bytes) != hipSuccess) return fail(IS_ERR_OOM, "embedding staging");
+    hipError_t e = hipSuccess;
+    for (int64_t r0 = 0; r0 < n && e == hipSuccess; r0 += piece_rows) {
+      const int64_t m = std::min(piece_rows, n - r0);
+      e = hipMemcpy(tmp, emb + r0 * s->emb_dim, (size_t)m * s->emb_dim * 2, from_dev);
+      if (e == hipSuccess) e = is::launch_emb_relayout(tmp, first + r0, m, s->emb_dim, s->emb, nullptr);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
+    }
+    (void)hipFree(tmp);
     if (e != hipSuccess) return hip_fail(e, "embedding load");
   }
   return IS_OK;
@@ -312,7 +337,7 @@ IS_EXPORT int is_store_get_info(const is_store* s, is_store_info* out) {
   out->hbm_kv_bytes = (int64_t)s->fact_bytes(0, s->n_hbm) * 2;
   out->host_kv_bytes = (int64_t)s->fact_bytes(s->n_hbm, s->n_facts) * 2;
   out->total_tokens = s->tok_off[s->n_facts];
-  out->emb_bytes = (int64_t)s->n_facts * s->emb_dim * 2;
+  out->emb_bytes = s->emb_rows() * s->emb_dim * 2;
   return IS_OK;
 }
 

@@ -45,6 +45,17 @@ struct TopkLaunch {
   float* scores;          // [n_q][k]
 };
 
+// Embedding layout in HBM.  For emb_dim % 64 == 0 the store keeps the
+// embeddings tile-blocked, [tile of 256 facts][64-dim chunk][256 rows][64],
+// rows past n_facts zero, so that every 256 x 64 block the scan streams is
+// one contiguous 32 KB span; otherwise row-major [n_facts][emb_dim].
+inline bool topk_blocked_layout(int32_t emb_dim) { return emb_dim % 64 == 0; }
+inline int64_t topk_padded_facts(int64_t n_facts) { return (n_facts + 255) / 256 * 256; }
+// Scatters rows [first, first + n) given row-major in device memory into the
+// blocked layout.
+hipError_t launch_emb_relayout(const uint16_t* rows, int64_t first, int64_t n,
+                               int32_t emb_dim, uint16_t* emb, hipStream_t stream);
+
 // Facts in the threshold sample for a store of n_facts facts.
 int64_t topk_sample_size(int64_t n_facts);
 // Scratch bytes for one call of n_q (<= 128) queries.

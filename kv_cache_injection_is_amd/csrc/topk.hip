@@ -299,6 +299,179 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The scan for emb_dim % 64 == 0 (tile-blocked embeddings): each 256-fact x
+// 64-dim block (32 KB, contiguous in HBM) and the matching query chunk go
+// from memory straight into a 3-stage LDS ring (global_load_lds_dwordx4, no
+// registers), so two chunks are in flight while the MFMAs of a third run.
+// A stage holds the tile's 256 rows and the block's 128 query rows as 8
+// 16-byte pieces each; piece p of row r sits at slot r*8 + (p ^ (r & 7)),
+// which spreads the 32 rows an MFMA fragment read touches over all banks.
+// Each DMA instruction fills 64 consecutive slots (1 KB) from 8 whole
+// 128-byte row segments.  The ring's waits are explicit (vmcnt), since the
+// compiler does not track these transfers.
+constexpr int kStages = 3;
+constexpr int kDmaKC = 64;                    // dims per chunk
+constexpr int kEPieces = kFT * kDmaKC / 8;    // 16-byte pieces of a stage's rows
+constexpr int kQPiecesDma = kQB * kDmaKC / 8;
+constexpr int kEDma = kEPieces / 64 / kWaves; // DMA instructions per wave per stage
+constexpr int kQDma = kQPiecesDma / 64 / kWaves;
+constexpr int kDmaPerStage = kEDma + kQDma;
+
+typedef __attribute__((address_space(3))) char* lds_cptr;
+
+struct DmaSmem {
+  u32x4 e[kStages][kEPieces];
+  u32x4 q[kStages][kQPiecesDma];
+};
+
+// One 16-byte piece per lane from `g` into LDS bytes [lds + 16*lane, +16).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(g) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool kSample>
+__global__ __launch_bounds__(kThreads) void topk_scan_dma(TopkLaunch a) {
+  __shared__ DmaSmem sm;
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int row = lane % 32;
+  const int grp = lane / 32;
+  const int qb0 = blockIdx.y * kQB;
+  const int D = a.emb_dim;
+  const int n_chunks = D / kDmaKC;
+  const int64_t limit = kSample ? a.sample_n : a.n_facts;
+  const int64_t n_tiles = (limit + kFT - 1) / kFT;
+  if ((int64_t)blockIdx.x >= n_tiles) return;
+  const int64_t my_tiles = (n_tiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const int64_t total = my_tiles * n_chunks;
+
+  float tau[4];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    const int q = qb0 + qt * 32 + row;
+    tau[qt] = (!kSample && q < a.n_q) ? a.tau[q] : 0.f;
+  }
+
+  const uint32_t e_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.e[0][0];
+  const uint32_t q_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.q[0][0];
+  // Chunk g of this workgroup's stream: tile blockIdx.x + (g / n_chunks) *
+  // gridDim.x, dims [(g % n_chunks) * 64, +64).
+  auto issue = [&](int64_t g) {
+    const int64_t t = blockIdx.x + (g / n_chunks) * gridDim.x;
+    const int c = (int)(g % n_chunks);
+    const int b = (int)(g % kStages);
+    // the tile's 256 x 64 block of the blocked layout: 32 KB contiguous
+    const uint16_t* blk = a.emb + (t * n_chunks + c) * (int64_t)(kFT * kDmaKC);
+#pragma unroll
+    for (int i = 0; i < kEDma; ++i) {
+      const int slot = (wave * kEDma + i) * 64 + lane;
+      const int r = slot / 8, piece = (slot % 8) ^ (r & 7);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          e_lds + (uint32_t)((b * kEPieces + (wave * kEDma + i) * 64) * 16));
+      dma16(blk + r * kDmaKC + piece * 8, dst);
+    }
+#pragma unroll
+    for (int i = 0; i < kQDma; ++i) {
+      const int slot = (wave * kQDma + i) * 64 + lane;
+      const int r = slot / 8, piece = (slot % 8) ^ (r & 7);
+      const uint16_t* src = qb0 + r < a.n_q ? a.q + (int64_t)(qb0 + r) * D + c * kDmaKC + piece * 8
+                                            : a.q;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          q_lds + (uint32_t)((b * kQPiecesDma + (wave * kQDma + i) * 64) * 16));
+      dma16(src, dst);
+    }
+  };
+
+  float16v acc[2][4];
+  auto zero_acc = [&] {
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[ft][qt][e] = 0.f;
+  };
+  // k-step s uses logical pieces 2s + grp of every row (both operands).
+  auto compute = [&](int b) {
+    const u32x4* es = sm.e[b];
+    const u32x4* qs = sm.q[b];
+#pragma unroll
+    for (int s = 0; s < kDmaKC / 16; ++s) {
+      const int x = (2 * s + grp) ^ (row & 7);
+      half8 av[2], bv[4];
+#pragma unroll
+      for (int ft = 0; ft < 2; ++ft)
+        av[ft] = __builtin_bit_cast(half8, es[(wave * kFTW + ft * 32 + row) * 8 + x]);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+        bv[qt] = __builtin_bit_cast(half8, qs[(qt * 32 + row) * 8 + x]);
+#pragma unroll
+      for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt)
+          acc[ft][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[ft], bv[qt], acc[ft][qt], 0, 0, 0);
+    }
+  };
+  auto emit = [&](int64_t t) {
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+      const int64_t fbase = t * kFT + wave * kFTW + ft * 32 + 4 * grp;
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const int q = qb0 + qt * 32 + row;
+        if (q >= a.n_q) continue;
+        if (kSample) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t f = fbase + 8 * (e / 4) + (e % 4);
+            if (f < limit) a.sample[(int64_t)q * a.sample_n + f] = acc[ft][qt][e];
+          }
+        } else {
+          uint32_t m = 0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t f = fbase + 8 * (e / 4) + (e % 4);
+            m |= (f < limit && acc[ft][qt][e] >= tau[qt]) ? (1u << e) : 0u;
+          }
+          if (m) {
+            uint32_t pos = atomicAdd(&a.count[q], (uint32_t)__builtin_popcount(m));
+            uint64_t* dst = a.cand + (int64_t)q * a.n_facts;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (m & (1u << e))
+                dst[pos++] = key_of(ord_of(acc[ft][qt][e]),
+                                    (uint32_t)(fbase + 8 * (e / 4) + (e % 4)));
+          }
+        }
+      }
+    }
+  };
+
+  for (int64_t g = 0; g < kStages - 1 && g < total; ++g) issue(g);
+  zero_acc();
+  for (int64_t g = 0; g < total; ++g) {
+    // chunk g's transfers are done once at most the later stages' are in flight
+    if (g + 1 < total) wait_vm<kDmaPerStage>(); else wait_vm<0>();
+    __syncthreads();   // every wave's transfers for chunk g landed; chunk g-1's buffer is free
+    if (g + kStages - 1 < total) issue(g + kStages - 1);
+    compute((int)(g % kStages));
+    if (g % n_chunks == n_chunks - 1) {
+      emit(blockIdx.x + (g / n_chunks) * gridDim.x);
+      zero_acc();
+    }
+  }
+  wait_vm<0>();
+}
+
 constexpr int kSelThreads = 256;
 
 // The k-th largest of n values (32- or 64-bit) in global memory, by
@@ -385,7 +558,30 @@ __global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
   }
 }
 
+__global__ __launch_bounds__(256) void emb_relayout(const uint16_t* __restrict__ rows,
+                                                   int64_t first, int64_t n, int32_t D,
+                                                   uint16_t* __restrict__ emb) {
+  const int pieces = D / 8;
+  const int n_chunks = D / kDmaKC;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * pieces) return;
+  const int64_t r = i / pieces;
+  const int p = (int)(i % pieces);
+  const int64_t f = first + r;
+  const int64_t dst = ((f / kFT * n_chunks + p / 8) * kFT + f % kFT) * kDmaKC + (p % 8) * 8;
+  *reinterpret_cast<u32x4*>(emb + dst) = *reinterpret_cast<const u32x4*>(rows + r * D + p * 8);
+}
+
 }  // namespace
+
+hipError_t launch_emb_relayout(const uint16_t* rows, int64_t first, int64_t n, int32_t emb_dim,
+                               uint16_t* emb, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t threads = n * (emb_dim / 8);
+  hipLaunchKernelGGL(emb_relayout, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     rows, first, n, emb_dim, emb);
+  return hipGetLastError();
+}
 
 int topk_workgroups(int64_t n_facts) {
   const int64_t tiles = (n_facts + kFT - 1) / kFT;
@@ -405,16 +601,16 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream) {
   const unsigned qblocks = (unsigned)((a.n_q + kQB - 1) / kQB);
   const dim3 g_sample((unsigned)topk_workgroups(a.sample_n), qblocks);
   const dim3 g_stream((unsigned)topk_workgroups(a.n_facts), qblocks);
-  if (a.emb_dim % 128 == 0) {
-    hipLaunchKernelGGL((topk_scan<128, true>), g_sample, dim3(kThreads), 0, stream, a);
+  if (a.emb_dim % kDmaKC == 0) {
+    hipLaunchKernelGGL((topk_scan_dma<true>), g_sample, dim3(kThreads), 0, stream, a);
   } else if (a.emb_dim % 32 == 0) {
     hipLaunchKernelGGL((topk_scan<32, true>), g_sample, dim3(kThreads), 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }
   hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
-  if (a.emb_dim % 128 == 0)
-    hipLaunchKernelGGL((topk_scan<128, false>), g_stream, dim3(kThreads), 0, stream, a);
+  if (a.emb_dim % kDmaKC == 0)
+    hipLaunchKernelGGL((topk_scan_dma<false>), g_stream, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((topk_scan<32, false>), g_stream, dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL(topk_final, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
