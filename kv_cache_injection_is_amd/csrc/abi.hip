@@ -47,6 +47,7 @@ struct Slot {
 };
 
 constexpr int kSlots = 4;
+constexpr int kTopkSlots = 2;
 
 }  // namespace
 
@@ -74,13 +75,15 @@ struct is_store {
   std::vector<uint64_t> v_addr;
   uint16_t* emb = nullptr;
   std::mutex mu;
-  Slot slots[kSlots];
+  Slot slots[kSlots];              // inject staging (device + pinned host)
   int next_slot = 0;
+  Slot topk_slots[kTopkSlots];     // top-k scratch (device only)
+  int next_topk_slot = 0;
 
   int64_t row_elems() const { return (int64_t)L * H * d; }
-  // Rows allocated for the embeddings (padded to whole tiles when blocked).
-  int64_t emb_rows() const {
-    return is::topk_blocked_layout(emb_dim) ? is::topk_padded_facts(n_facts) : n_facts;
+  // Bytes of the blocked embeddings (whole tiles, padded width).
+  size_t emb_bytes() const {
+    return (size_t)is::topk_padded_facts(n_facts) * is::topk_padded_dim(emb_dim) * 2;
   }
   size_t fact_bytes(int64_t f0, int64_t f1) const {
     return (size_t)(tok_off[f1] - tok_off[f0]) * row_elems() * es;
@@ -112,11 +115,15 @@ namespace {
 void free_store(is_store* s) {
   if (s == nullptr) return;
   DeviceGuard g(s->device);
-  for (Slot& sl : s->slots) {
-    if (sl.done) (void)hipEventSynchronize(sl.done);
-    if (sl.dev) (void)hipFree(sl.dev);
-    if (sl.host) (void)hipHostFree(sl.host);
-    if (sl.done) (void)hipEventDestroy(sl.done);
+  for (Slot* ring : {s->slots, s->topk_slots}) {
+    const int n = ring == s->slots ? kSlots : kTopkSlots;
+    for (int i = 0; i < n; ++i) {
+      Slot& sl = ring[i];
+      if (sl.done) (void)hipEventSynchronize(sl.done);
+      if (sl.dev) (void)hipFree(sl.dev);
+      if (sl.host) (void)hipHostFree(sl.host);
+      if (sl.done) (void)hipEventDestroy(sl.done);
+    }
   }
   if (s->k_dev) (void)hipFree(s->k_dev);
   if (s->v_dev) (void)hipFree(s->v_dev);
@@ -130,9 +137,11 @@ void free_store(is_store* s) {
 
 // Takes the next staging slot with room for `bytes`, after the work that
 // last used it has finished.  Caller holds s->mu.
-int acquire_slot(is_store* s, size_t bytes, Slot** out) {
-  Slot& sl = s->slots[s->next_slot];
-  s->next_slot = (s->next_slot + 1) % kSlots;
+// Takes the next slot of a ring once the work that last used it is done,
+// growing its buffers to `bytes` (and a pinned host mirror when `host`).
+int acquire(Slot* ring, int n, int* next, size_t bytes, bool host, Slot** out) {
+  Slot& sl = ring[*next];
+  *next = (*next + 1) % n;
   hipError_t e;
   if (sl.done == nullptr) {
     if ((e = hipEventCreateWithFlags(&sl.done, hipEventDisableTiming)) != hipSuccess)
@@ -147,7 +156,7 @@ int acquire_slot(is_store* s, size_t bytes, Slot** out) {
     sl.cap = 0;
     const size_t cap = std::max<size_t>(bytes + bytes / 4, 1 << 16);
     if (hipMalloc(&sl.dev, cap) != hipSuccess) return fail(IS_ERR_OOM, "staging hipMalloc");
-    if (hipHostMalloc(&sl.host, cap, hipHostMallocDefault) != hipSuccess) {
+    if (host && hipHostMalloc(&sl.host, cap, hipHostMallocDefault) != hipSuccess) {
       (void)hipFree(sl.dev);
       sl.dev = nullptr;
       return fail(IS_ERR_OOM, "staging hipHostMalloc");
@@ -156,6 +165,14 @@ int acquire_slot(is_store* s, size_t bytes, Slot** out) {
   }
   *out = &sl;
   return IS_OK;
+}
+
+int acquire_slot(is_store* s, size_t bytes, Slot** out) {
+  return acquire(s->slots, kSlots, &s->next_slot, bytes, true, out);
+}
+
+int acquire_topk_slot(is_store* s, size_t bytes, Slot** out) {
+  return acquire(s->topk_slots, kTopkSlots, &s->next_topk_slot, bytes, false, out);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -251,7 +268,7 @@ IS_EXPORT int is_store_create(const is_store_desc* d, is_store** out) {
     }
   }
   if (s->emb_dim > 0) {
-    const size_t bytes = (size_t)s->emb_rows() * s->emb_dim * 2;
+    const size_t bytes = s->emb_bytes();
     if (hipMalloc((void**)&s->emb, bytes) != hipSuccess) {
       free_store(s);
       return fail(IS_ERR_OOM, "device allocation of the embeddings failed");
@@ -307,10 +324,7 @@ IS_EXPORT int is_store_load(is_store* s, int64_t first, int64_t n, const void* k
       f = g;
     }
   }
-  if (emb && !is::topk_blocked_layout(s->emb_dim)) {
-    hipError_t e = hipMemcpy(s->emb + first * s->emb_dim, emb, (size_t)n * s->emb_dim * 2, from_dev);
-    if (e != hipSuccess) return hip_fail(e, "embedding load");
-  } else if (emb) {
+  if (emb) {
     // rows to device memory in pieces, then scattered into the blocked layout
     const int64_t piece_rows = 65536;
     uint16_t* tmp = nullptr;
@@ -337,7 +351,7 @@ IS_EXPORT int is_store_get_info(const is_store* s, is_store_info* out) {
   out->hbm_kv_bytes = (int64_t)s->fact_bytes(0, s->n_hbm) * 2;
   out->host_kv_bytes = (int64_t)s->fact_bytes(s->n_hbm, s->n_facts) * 2;
   out->total_tokens = s->tok_off[s->n_facts];
-  out->emb_bytes = s->emb_rows() * s->emb_dim * 2;
+  out->emb_bytes = s->emb_dim > 0 ? (int64_t)s->emb_bytes() : 0;
   return IS_OK;
 }
 
@@ -449,30 +463,28 @@ IS_EXPORT int is_topk(const is_store* cs, const uint16_t* q, int32_t n_q, int32_
   DeviceGuard guard(s->device);
   std::lock_guard<std::mutex> lock(s->mu);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // Queries go in groups of up to 128 (one query block per scan).
+  // Queries go in groups of up to 128 (one scan launch each).
   for (int32_t q0 = 0; q0 < n_q; q0 += 128) {
     const int32_t nq = std::min<int32_t>(128, n_q - q0);
+    const is::TopkScratch lay = is::topk_scratch(s->n_facts, nq, s->emb_dim);
+    Slot* sl = nullptr;
+    int rc = acquire_topk_slot(s, lay.bytes, &sl);
+    if (rc != IS_OK) return rc;
+    char* p = static_cast<char*>(sl->dev);
     is::TopkLaunch a{};
     a.emb = s->emb;
     a.q = q + (int64_t)q0 * s->emb_dim;
     a.n_facts = s->n_facts;
-    a.sample_n = is::topk_sample_size(s->n_facts);
     a.emb_dim = s->emb_dim;
     a.n_q = nq;
     a.k = k;
+    a.q_pad = reinterpret_cast<uint16_t*>(p + lay.q_off);
+    a.gmax = reinterpret_cast<uint32_t*>(p + lay.gmax_off);
+    a.tau = reinterpret_cast<float*>(p + lay.tau_off);
+    a.count = reinterpret_cast<uint32_t*>(p + lay.count_off);
+    a.cand = reinterpret_cast<uint64_t*>(p + lay.cand_off);
     a.ids = ids + (int64_t)q0 * k;
     a.scores = scores + (int64_t)q0 * k;
-    Slot* sl = nullptr;
-    int rc = acquire_slot(s, is::topk_scratch_bytes(s->n_facts, nq), &sl);
-    if (rc != IS_OK) return rc;
-    char* p = static_cast<char*>(sl->dev);
-    a.sample = reinterpret_cast<float*>(p);
-    p += align256((size_t)nq * a.sample_n * 4);
-    a.tau = reinterpret_cast<float*>(p);
-    p += align256((size_t)nq * 4);
-    a.count = reinterpret_cast<uint32_t*>(p);
-    p += align256((size_t)nq * 4);
-    a.cand = reinterpret_cast<uint64_t*>(p);
     hipError_t e = is::launch_topk(a, st);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
     e = hipEventRecord(sl->done, st);
