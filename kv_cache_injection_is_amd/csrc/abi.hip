@@ -394,15 +394,23 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
                            max_blocks, cache, rope, &items, &n_tokens);
   if (rc != IS_OK) return rc;
   if (items.empty()) return IS_OK;
-#ifndef IS_SORT_WORK
-#define IS_SORT_WORK 1
-#endif
-#if IS_SORT_WORK
-  // Launch order only: workgroups then sweep the store in address order.
-  std::sort(items.begin(), items.end(), [](const is::WorkItem& x, const is::WorkItem& y) {
-    return x.tier != y.tier ? x.tier < y.tier : x.k < y.k;
-  });
-#endif
+  // Launch order only: by fact id (stable), which is the store's layout
+  // order (HBM facts, then the host tier, each in id order), so the
+  // workgroups sweep the store front to back.  LSD radix sort, 11-bit digits.
+  thread_local std::vector<uint32_t> order, spare;
+  const uint32_t n_items = (uint32_t)items.size();
+  order.resize(n_items);
+  spare.resize(n_items);
+  for (uint32_t i = 0; i < n_items; ++i) order[i] = i;
+  const uint32_t max_id = (uint32_t)(s->n_facts - 1);
+  for (int shift = 0; shift == 0 || (shift < 32 && (max_id >> shift) != 0); shift += 11) {
+    uint32_t hist[2049] = {};
+    for (uint32_t i = 0; i < n_items; ++i) ++hist[(((uint32_t)fact_ids[order[i]] >> shift) & 2047u) + 1];
+    for (int b = 0; b < 2048; ++b) hist[b + 1] += hist[b];
+    for (uint32_t i = 0; i < n_items; ++i)
+      spare[hist[((uint32_t)fact_ids[order[i]] >> shift) & 2047u]++] = order[i];
+    order.swap(spare);
+  }
   is::plan_rope(s->d, rope, &g);
   const size_t items_bytes = align256(items.size() * sizeof(is::WorkItem));
   const size_t bt_bytes = align256((size_t)n_req * max_blocks * sizeof(int32_t));
@@ -414,7 +422,8 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
   rc = acquire_slot(s, total, &sl);
   if (rc != IS_OK) return rc;
   char* h = static_cast<char*>(sl->host);
-  std::memcpy(h, items.data(), items.size() * sizeof(is::WorkItem));
+  is::WorkItem* h_items = reinterpret_cast<is::WorkItem*>(h);
+  for (uint32_t i = 0; i < n_items; ++i) h_items[i] = items[order[i]];
   std::memcpy(h + items_bytes, block_tables, (size_t)n_req * max_blocks * sizeof(int32_t));
   std::memcpy(h + items_bytes + bt_bytes, g.data(), g.size() * sizeof(float));
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -119,6 +119,48 @@ struct SlotRun {   // slots [first, last] of one physical block
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Slot-overlap check over a bitmap of the cache's slots (bit blk * B + s),
+// for caches up to kBitmapSlots slots; larger ones sort the runs instead.
+constexpr int64_t kBitmapSlots = int64_t(1) << 30;
+
+// Sets bits [b0, b1]; returns true if one of them was set already.
+bool mark_bits(std::vector<uint64_t>& bits, int64_t b0, int64_t b1) {
+  bool clash = false;
+  for (int64_t w = b0 >> 6; w <= (b1 >> 6); ++w) {
+    const int lo = w == (b0 >> 6) ? (int)(b0 & 63) : 0;
+    const int hi = w == (b1 >> 6) ? (int)(b1 & 63) : 63;
+    const uint64_t m = (hi == 63 ? ~uint64_t(0) : (uint64_t(1) << (hi + 1)) - 1) & (~uint64_t(0) << lo);
+    clash |= (bits[w] & m) != 0;
+    bits[w] |= m;
+  }
+  return clash;
+}
+
+// True if two runs share a slot.  The bitmap is all zero between calls.
+bool runs_overlap(const std::vector<SlotRun>& runs, int64_t B, int64_t n_blocks) {
+  if (n_blocks * B > kBitmapSlots) {
+    std::vector<SlotRun> sorted(runs);
+    std::sort(sorted.begin(), sorted.end());
+    for (size_t i = 1; i < sorted.size(); ++i)
+      if (sorted[i].block == sorted[i - 1].block && sorted[i].first <= sorted[i - 1].last)
+        return true;
+    return false;
+  }
+  thread_local std::vector<uint64_t> tl_bits;
+  std::vector<uint64_t>& bits = tl_bits;
+  const size_t words = (size_t)((n_blocks * B + 63) >> 6);
+  if (bits.size() < words) bits.resize(words, 0);
+  size_t i = 0;
+  bool clash = false;
+  for (; i < runs.size() && !clash; ++i)
+    clash = mark_bits(bits, runs[i].block * B + runs[i].first, runs[i].block * B + runs[i].last);
+  for (size_t j = 0; j < i; ++j)   // clear every word touched
+    for (int64_t w = (runs[j].block * B + runs[j].first) >> 6;
+         w <= ((runs[j].block * B + runs[j].last) >> 6); ++w)
+      bits[w] = 0;
+  return clash;
+}
+
 }  // namespace
 
 int plan_inject(const StoreGeom& g, int32_t n_req, const int32_t* req_off,
@@ -163,7 +205,9 @@ int plan_inject(const StoreGeom& g, int32_t n_req, const int32_t* req_off,
                                       std::to_string(j) + " is outside [0, n_facts)");
 
   const int64_t B = c->block_size;
-  std::vector<SlotRun> runs;
+  thread_local std::vector<SlotRun> tl_runs;
+  std::vector<SlotRun>& runs = tl_runs;
+  runs.clear();
   int64_t total = 0;
   if (items) {
     items->clear();
@@ -201,11 +245,8 @@ int plan_inject(const StoreGeom& g, int32_t n_req, const int32_t* req_off,
       runs.push_back(SlotRun{blk, (int32_t)lo, (int32_t)hi});
     }
   }
-  std::sort(runs.begin(), runs.end());
-  for (size_t i = 1; i < runs.size(); ++i)
-    if (runs[i].block == runs[i - 1].block && runs[i].first <= runs[i - 1].last)
-      return fail(IS_ERR_SLOT_OVERLAP, "two injected tokens map to a slot of block " +
-                                           std::to_string(runs[i].block));
+  if (runs_overlap(runs, B, c->n_blocks))
+    return fail(IS_ERR_SLOT_OVERLAP, "two injected tokens of the call map to the same cache slot");
   if (n_tokens) *n_tokens = total;
   return IS_OK;
 }

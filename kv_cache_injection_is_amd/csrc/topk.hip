@@ -29,10 +29,11 @@
 // every 256-fact x 64-dim block is one contiguous 32 KB span.  A persistent
 // workgroup (4 waves, one per SIMD) streams its tiles' blocks, and the
 // matching 128 x 64 query chunk, from memory straight into a 3-stage LDS
-// ring with global_load_lds_dwordx4 (no registers on the way), so two chunks
-// are in flight while the MFMAs of a third run.  Each wave owns 64 facts of
-// the tile (two 32-row tiles of v_mfma_f32_32x32x16_f16, fp32 accumulation)
-// against all 128 queries.
+// ring with global_load_lds_dwordx4 (no registers on the way).  Each wave
+// owns 64 facts of the tile (two 32-row tiles of v_mfma_f32_32x32x16_f16,
+// fp32 accumulation) against all 128 queries, and loads those 64 rows
+// itself, so it refills its part of a buffer without waiting for the other
+// waves: the fact rows of three chunks can be in flight while it waits.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -56,7 +57,6 @@ constexpr int kEPieces = kFT * kKC / 8;   // 16-byte pieces of a stage's fact ro
 constexpr int kQPieces = kQB * kKC / 8;   // ... and of its query rows
 constexpr int kEDma = kEPieces / 64 / kWaves;   // DMA instructions per wave per stage
 constexpr int kQDma = kQPieces / 64 / kWaves;
-constexpr int kDmaPerStage = kEDma + kQDma;
 static_assert(kFT == kTopkTile, "tile size");
 
 // Order-preserving map of a float to uint32 (larger float -> larger code).
@@ -198,34 +198,44 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
 
   const uint32_t e_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.e[0][0];
   const uint32_t q_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.q[0][0];
-  // Issue cursor: tile it, chunk ic, ring buffer ib.
-  int64_t it = w;
-  int ic = 0, ib = 0;
-  auto issue = [&]() {
+  // Wave w's transfers fill exactly the fact rows [64w, 64w + 64) that its
+  // own MFMAs read, so it may refill its part of a ring buffer as soon as it
+  // has finished with it; the query rows are read by every wave and wait for
+  // the barrier.
+  // Fact cursor: tile et, chunk ec, ring buffer eb.
+  int64_t et = w;
+  int ec = 0, eb = 0;
+  auto issue_e = [&]() {
     // the tile's 256 x 64 block of the blocked layout: 32 KB contiguous
-    const uint16_t* blk = a.emb + (it * n_chunks + ic) * (int64_t)(kFT * kKC);
+    const uint16_t* blk = a.emb + (et * n_chunks + ec) * (int64_t)(kFT * kKC);
 #pragma unroll
     for (int i = 0; i < kEDma; ++i) {
       const int s0 = (wave * kEDma + i) * 64;
       const int slot = s0 + lane;
       const int r = slot >> 3, p = (slot & 7) ^ ((r >> 1) & 7);
       dma16(blk + r * kKC + p * 8,
-            __builtin_amdgcn_readfirstlane(e_lds + (uint32_t)((ib * kEPieces + s0) * 16)));
+            __builtin_amdgcn_readfirstlane(e_lds + (uint32_t)((eb * kEPieces + s0) * 16)));
     }
+    if (++ec == n_chunks) {
+      ec = 0;
+      et += G;
+    }
+    if (++eb == kStages) eb = 0;
+  };
+  // Query cursor: chunk qc, ring buffer qb.
+  int qc = 0, qb = 0;
+  auto issue_q = [&]() {
 #pragma unroll
     for (int i = 0; i < kQDma; ++i) {
       const int s0 = (wave * kQDma + i) * 64;
       const int slot = s0 + lane;
       const int r = slot >> 3, p = (slot & 7) ^ ((r >> 1) & 7);
       // rows past n_q re-load row 0; their scores are never used
-      const uint16_t* src = a.q + (int64_t)(r < a.n_q ? r : 0) * D + ic * kKC + p * 8;
-      dma16(src, __builtin_amdgcn_readfirstlane(q_lds + (uint32_t)((ib * kQPieces + s0) * 16)));
+      const uint16_t* src = a.q + (int64_t)(r < a.n_q ? r : 0) * D + qc * kKC + p * 8;
+      dma16(src, __builtin_amdgcn_readfirstlane(q_lds + (uint32_t)((qb * kQPieces + s0) * 16)));
     }
-    if (++ic == n_chunks) {
-      ic = 0;
-      it += G;
-    }
-    if (++ib == kStages) ib = 0;
+    if (++qc == n_chunks) qc = 0;
+    if (++qb == kStages) qb = 0;
   };
 
   float16v acc[2][4];
@@ -267,15 +277,29 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
     }
   };
 
-  for (int g = 0; g < kStages - 1 && g < total; ++g) issue();
+  static_assert(kStages == 3, "the wait counts below assume three ring buffers");
+  for (int g = 0; g < kStages - 1 && g < total; ++g) {
+    issue_e();
+    issue_q();
+  }
   // Compute cursor: tile ct, chunk cc, ring buffer cb.
   int64_t ct = w;
   int cc = 0, cb = 0;
   for (int g = 0; g < total; ++g) {
-    // chunk g's transfers are done once at most the next stage's are in flight
-    if (g + 1 < total) wait_vm<kDmaPerStage>(); else wait_vm<0>();
-    ring_barrier();   // every wave's transfers for chunk g landed; chunk g-1's buffer is free
-    if (g + kStages - 1 < total) issue();
+    // Chunk g+2's fact rows go into the buffer this wave finished with in
+    // chunk g-1.  Issued after chunk g's query rows: the fact rows of g+1
+    // and g+2 and the query rows of g+1 (20 transfers), so chunk g has
+    // landed once at most that many are in flight (loads complete in order).
+    if (g + 2 < total) {
+      issue_e();
+      wait_vm<2 * kEDma + kQDma>();
+    } else if (g + 1 < total) {
+      wait_vm<kEDma + kQDma>();
+    } else {
+      wait_vm<0>();
+    }
+    ring_barrier();   // every wave's transfers for chunk g landed; chunk g-1's query rows are free
+    if (g + 2 < total) issue_q();
     if (cc == 0)
       mma_chunk<true>(sm.e[cb], sm.q[cb], wave, row, grp, acc);
     else

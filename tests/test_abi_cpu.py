@@ -124,3 +124,23 @@ def test_empty_call_is_ok():
     z = np.zeros((0, 1), np.int32)
     assert K.is_inject_check(d, np.array([0], np.int32), np.zeros(0, np.int32),
                              np.zeros(0, np.int32), z, _cache(), ROPE) == 0
+
+
+@pytest.mark.parametrize("nb,B,bt,ok,bad", [
+    # small cache (slot bitmap): runs of 40-slot blocks straddle 64-bit words
+    (16, 40, [[2, 3], [3, 0]], [0, 10], [0, 9]),
+    # 2^31 slots: the check sorts the runs instead
+    (1 << 21, 1024, [[3, 0], [3, 0]], [0, 50], [0, 49]),
+])
+def test_slot_overlap_check_each_path_and_state_is_cleared(nb, B, bt, ok, bad):
+    d, keep = _desc(lens=(50, 30))
+    req_off = np.array([0, 1, 2], np.int32)
+    ids = np.array([0, 1], np.int32)
+    bt = np.array(bt, np.int32)
+    c = _cache(nb=nb, B=B)
+    ok = np.array(ok, np.int32)
+    assert K.is_inject_check(d, req_off, ids, ok, bt, c, ROPE) == 80
+    assert _code(lambda: K.is_inject_check(d, req_off, ids, np.array(bad, np.int32), bt, c,
+                                           ROPE)) == -4
+    # the failed call leaves nothing behind: the clean call passes again
+    assert K.is_inject_check(d, req_off, ids, ok, bt, c, ROPE) == 80
