@@ -10,8 +10,9 @@ before the timed region.
 
 Prints one JSON line: injected tokens/s for the whole step, plus the
 inject kernel's roofline (algorithmic bytes / HIP-event kernel time against
-8 TB/s), the top-k rate, and the fp64 CPU oracle timed on a bounded sample
-of the same workload.
+8 TB/s), the top-k rate (back to back, and with the caches flushed before
+each call), the top-k rate over the Qwen-shaped 1M x 1024 embeddings, and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -55,6 +56,55 @@ def traffic_from_counters(n_launch_bytes: float):
         return None
     m = re.search(r"inject_traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     return float(m.group(1)) if m else None
+
+
+def topk_cold(torch, stream, flush, fn, reps: int) -> float:
+    """Median time of `fn` on `stream`, each call preceded by a 1 GiB write
+    that evicts the L2 and Infinity Cache (HIP events around the call)."""
+    times = []
+    for i in range(reps):
+        flush.fill_(i & 255)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
+
+
+def topk_large(torch, K, W, Hn, stream, flush, reps: int) -> dict:
+    """Top-50 for 100 queries over the 1M x 1024 fp16 embeddings of the
+    Qwen2.5-7B-shaped workload (2.05 GB); its K/V store is not needed for
+    top-k, so a one-layer, one-head store of one-token facts carries it."""
+    base = W.WORKLOADS["qwen7b_offload"]
+    w = base.scaled(name="qwen7b_topk", n_layers=1, n_kv_heads=1, head_dim=32,
+                    len_dist=("uniform", 1, 1), host_fraction=0.0)
+    st = Hn.make_store(w)
+    q = torch.from_numpy(W.query_embeddings(w).view(np.int16)).cuda()
+    n_q, k = w.n_req, w.k
+    ids = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((n_q, k), dtype=torch.float32, device="cuda")
+    call = lambda: K.is_topk(st.handle, q, n_q, k, ids, sc, stream)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm = e0.elapsed_time(e1) / reps
+    cold = topk_cold(torch, stream, flush, call, reps)
+    st.destroy()
+    nbytes = w.n_facts * w.emb_dim * 2 + n_q * w.emb_dim * 2 + n_q * k * 8
+    gb = lambda ms: nbytes / (ms / 1e3) / 1e9
+    return {"workload": f"{w.n_facts} x {w.emb_dim} fp16 embeddings, {n_q} queries, top-{k}",
+            "ms": round(warm, 4), "GBps": round(gb(warm), 1),
+            "frac_of_8TBps": round(gb(warm) / HBM_PEAK_GBPS, 4),
+            "ms_cold": round(cold, 4), "GBps_cold": round(gb(cold), 1),
+            "queries_per_s": round(n_q / (warm / 1e3), 1)}
 
 
 def copy_bandwidth(torch, gib: float = 4.0, reps: int = 5) -> float:
@@ -128,12 +178,16 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mistral7b_batch")
     ap.add_argument("--cpu-sample", type=int, default=16,
                     help="requests in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the plain copy used to calibrate counters")
+    ap.add_argument("--topk-1m-only", action="store_true",
+                    help="only run the top-k over 1M x 1024 embeddings (for profiling)")
+    ap.add_argument("--skip-topk-1m", action="store_true",
+                    help="leave out the top-k over 1M x 1024 embeddings")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the path on a single MI355X; "
@@ -152,6 +206,13 @@ def main() -> int:
     import kv_cache_injection_is_amd as K
     from synth import workloads as W
     from tests import harness as Hn
+
+    if args.topk_1m_only:
+        stream = torch.cuda.current_stream()
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        print(json.dumps({"topk_1m": topk_large(torch, K, W, Hn, stream, flush,
+                                                max(args.steps, 2))}), flush=True)
+        return 0
 
     w = W.WORKLOADS[args.workload]
     log(f"workload {w.name}: building store ({w.n_facts} facts)")
@@ -193,13 +254,19 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
+    marks = []
     t0 = time.perf_counter()
     for i in range(args.steps):
+        marks.append(time.perf_counter())
         flat = step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    marks.append(t1)
     assert np.array_equal(flat, flat0), "retrieval changed between steps"
     ms_step = (t1 - t0) * 1e3 / args.steps
+    # step i's interval runs from its start to the next step's start (each
+    # step waits for the previous inject when it synchronizes on its ids)
+    step_ms = np.diff(np.array(marks)) * 1e3
 
     # Per-kernel times: the same calls launched back to back on the same
     # stream, bracketed by HIP events (host planning overlaps the previous
@@ -218,6 +285,10 @@ def main() -> int:
                                           stream), max(args.steps, 5))
     topk_ms = timed(lambda: K.is_topk(st.handle, q, n_q, k, ids_d, sc_d, stream),
                     max(args.steps, 5))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    topk_cold_ms = topk_cold(torch, stream, flush,
+                             lambda: K.is_topk(st.handle, q, n_q, k, ids_d, sc_d, stream),
+                             max(args.steps, 5))
 
     bytes_per_token = 4 * w.token_bytes           # K and V, read and written
     inj_bytes = tokens * bytes_per_token
@@ -239,6 +310,12 @@ def main() -> int:
         cpu = {"value": round(v, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
                "sample": desc}
     st.destroy()
+    del cache
+    topk_1m = None
+    if not args.skip_topk_1m:
+        log("top-k over 1M x 1024 embeddings")
+        topk_1m = topk_large(torch, K, W, Hn, stream, flush, max(args.steps, 5))
+        log(f"top-k 1M: {topk_1m['ms']:.3f} ms warm, {topk_1m['ms_cold']:.3f} ms cold")
 
     out = {
         "metric": METRIC,
@@ -248,6 +325,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, p)), 4) for p in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -278,8 +356,11 @@ def main() -> int:
                    "tokens_per_s": round(tokens / (inject_ms / 1e3), 1)},
         "topk": {"queries_per_s": round(n_q / (topk_ms / 1e3), 1), "GBps": round(topk_gbps, 1),
                  "ms": round(topk_ms, 4), "frac_of_8TBps": round(topk_gbps / HBM_PEAK_GBPS, 4),
-                 "note": "back-to-back launches; the 102 MB of embeddings may stay in the "
-                         "256 MB Infinity Cache between launches"},
+                 "ms_cold": round(topk_cold_ms, 4),
+                 "note": "ms: back-to-back launches (the 102 MB of embeddings may stay in the "
+                         "256 MB Infinity Cache); ms_cold: median with a 1 GiB write before "
+                         "each call"},
+        "topk_1m": topk_1m,
         "copy_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
     }
