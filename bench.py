@@ -107,6 +107,67 @@ def topk_large(torch, K, W, Hn, stream, flush, reps: int) -> dict:
             "queries_per_s": round(n_q / (warm / 1e3), 1)}
 
 
+def median_ms(torch, fn, reps: int) -> float:
+    """Median wall time of `fn` (which ends with a stream synchronize)."""
+    for _ in range(3):
+        fn()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        times.append((time.perf_counter() - t0) * 1e3)
+    return float(np.median(times))
+
+
+def device_path(torch, K, st, w, q, stream, cdesc, rope, prefix, bt, tokens, reps: int) -> dict:
+    """is_retrieve_inject: the batch step without the host round trip, and
+    the latency of one request at k = 5 and k = 50 on both paths (wall
+    clock from the call to the completed stream)."""
+    status = torch.full((1,), 1, dtype=torch.int32, device="cuda")
+    d_prefix = torch.from_numpy(np.ascontiguousarray(prefix, np.int32)).cuda()
+    d_bt = torch.from_numpy(np.ascontiguousarray(bt, np.int32)).cuda()
+    n_q, k = w.n_req, w.k
+
+    def batch():
+        K.is_retrieve_inject(st.handle, q, n_q, k, d_prefix, d_bt, cdesc, rope, status, None,
+                             stream)
+        stream.synchronize()
+
+    step = median_ms(torch, batch, reps)
+    assert int(status.item()) == 0, "device-side validation failed"
+    lat = {}
+    ids_h = torch.empty((1, 64), dtype=torch.int32, pin_memory=True)
+    req_off = None
+    for kk in (5, 50):
+        ids_d = torch.empty((1, kk), dtype=torch.int32, device="cuda")
+        sc_d = torch.empty((1, kk), dtype=torch.float32, device="cuda")
+        req_off = np.array([0, kk], np.int32)
+
+        def host():
+            K.is_topk(st.handle, q[:1], 1, kk, ids_d, sc_d, stream)
+            ids_h[:, :kk].copy_(ids_d, non_blocking=True)
+            stream.synchronize()
+            K.is_inject(st.handle, req_off, ids_h[0, :kk].numpy(), prefix[:1], bt[:1], cdesc,
+                        rope, stream)
+            stream.synchronize()
+
+        def dev():
+            K.is_retrieve_inject(st.handle, q[:1], 1, kk, d_prefix[:1], d_bt[:1], cdesc, rope,
+                                 status, None, stream)
+            stream.synchronize()
+
+        t_host = median_ms(torch, host, reps)
+        t_dev = median_ms(torch, dev, reps)
+        assert int(status.item()) == 0, "device-side validation failed"
+        toks = int(st.lens[ids_h[0, :kk].numpy()].sum())
+        lat[f"k{kk}"] = {"tokens": toks, "host_path_ms": round(t_host, 4),
+                         "device_path_ms": round(t_dev, 4)}
+    return {"step_ms": round(step, 4), "tokens_per_s": round(tokens / (step / 1e3), 1),
+            "latency_one_request": lat,
+            "note": "is_retrieve_inject: top-k, composition, validation and inject on the "
+                    "device; median wall time per call including the final synchronize"}
+
+
 def copy_bandwidth(torch, gib: float = 4.0, reps: int = 5) -> float:
     """Plain device copy (read + write) in GB/s."""
     n = int(gib * (1 << 30))
@@ -299,6 +360,14 @@ def main() -> int:
     log(f"step {ms_step:.3f} ms; inject {inject_ms:.3f} ms ({inj_gbps:.0f} GB/s); "
         f"top-k {topk_ms:.3f} ms")
 
+    dev = device_path(torch, K, st, w, q, stream, cdesc, rope, prefix, bt, tokens,
+                      max(args.steps, 10))
+    log(f"device path: step {dev['step_ms']:.3f} ms; one request k=5 "
+        f"{dev['latency_one_request']['k5']['device_path_ms']:.3f} ms "
+        f"(host path {dev['latency_one_request']['k5']['host_path_ms']:.3f}), k=50 "
+        f"{dev['latency_one_request']['k50']['device_path_ms']:.3f} ms "
+        f"(host path {dev['latency_one_request']['k50']['host_path_ms']:.3f})")
+
     copy_gbps = copy_bandwidth(torch)
     traffic = traffic_from_counters(inj_bytes)
 
@@ -361,6 +430,7 @@ def main() -> int:
                          "256 MB Infinity Cache); ms_cold: median with a 1 GiB write before "
                          "each call"},
         "topk_1m": topk_1m,
+        "device_path": dev,
         "copy_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
     }

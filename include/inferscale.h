@@ -209,6 +209,42 @@ int is_inject(const is_store* s, int32_t n_req, const int32_t* req_off,
               const is_cache* cache, const is_rope* rope, void* stream);
 
 /*
+ * Retrieve-and-inject without a host round trip: for each request r, the
+ * top-k facts of its query (as is_topk), laid out in rank order as one
+ * contiguous segment from serving position prefix_len[r] on and injected
+ * as by is_inject -- composition, validation and injection all run on the
+ * device, on `stream`, so the ids never travel to the host.  (Online phase:
+ * retrieved facts composed into one segment and injected into the paged
+ * cache.)
+ *   q_f16[n_req][emb_dim]        device, fp16 bits, 16-byte aligned
+ *   prefix_len[n_req]            device
+ *   block_tables[n_req][max_blocks]  device; read by the kernels, so it must
+ *                                stay valid until the stream has completed
+ *   ids_out[n_req][k]            device, optional (NULL): the selected ids
+ *   status                       device int32, written on the stream:
+ *                                IS_OK, or the smallest (most negative) code
+ *                                among the failed checks -- IS_ERR_FACT_ID,
+ *                                IS_ERR_BLOCK_TABLE (table too short or an
+ *                                entry outside [0, n_blocks)),
+ *                                IS_ERR_SLOT_OVERLAP (two injected tokens of
+ *                                the call share a slot), IS_ERR_INVALID_ARG
+ *                                (negative prefix, positions reaching 2^24).
+ *                                When it is not IS_OK no cache element is
+ *                                written.
+ * Returns before the work completes; host-side checks (store, k, cache
+ * geometry and alignment, rope, pointers) fail with the return code and
+ * enqueue nothing.  Requires 1 <= k <= min(64, n_facts), an embedding
+ * index, and a cache of at most 2^32 slots (the slot check keeps a
+ * bitmap of slots / 8 bytes).
+ * Errors: IS_ERR_INVALID_ARG, IS_ERR_UNSUPPORTED, IS_ERR_DTYPE,
+ * IS_ERR_ALIGN, IS_ERR_OOM, IS_ERR_HIP.
+ */
+int is_retrieve_inject(const is_store* s, const uint16_t* q_f16, int32_t n_req, int32_t k,
+                       const int32_t* prefix_len, const int32_t* block_tables,
+                       int32_t max_blocks, const is_cache* cache, const is_rope* rope,
+                       int32_t* ids_out, int32_t* status, void* stream);
+
+/*
  * The host half of is_inject on its own: validation and composition
  * against a store description (no store, no GPU).  Returns the status
  * is_inject would return for the same arguments before any device work,

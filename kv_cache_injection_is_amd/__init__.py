@@ -25,7 +25,7 @@ IS_DTYPE_F32, IS_DTYPE_BF16 = 0, 1
 IS_ROPE_NONE, IS_ROPE_LLAMA3 = 0, 1
 
 EXPORTS = ("is_store_create", "is_store_load", "is_store_get_info", "is_topk", "is_inject",
-           "is_inject_check", "is_store_destroy", "is_last_error")
+           "is_retrieve_inject", "is_inject_check", "is_store_destroy", "is_last_error")
 
 
 class ISError(RuntimeError):
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.is_topk.argtypes = [P, P, c.c_int32, c.c_int32, P, P, P]
         L.is_inject.argtypes = [P, c.c_int32, P, P, P, P, c.c_int32, c.POINTER(is_cache),
                                 c.POINTER(is_rope), P]
+        L.is_retrieve_inject.argtypes = [P, P, c.c_int32, c.c_int32, P, P, c.c_int32,
+                                         c.POINTER(is_cache), c.POINTER(is_rope), P, P, P]
         L.is_inject_check.argtypes = [c.POINTER(is_store_desc), c.c_int32, P, P, P, P,
                                       c.c_int32, c.POINTER(is_cache), c.POINTER(is_rope),
                                       c.POINTER(c.c_int64)]
@@ -171,6 +173,18 @@ def is_store_get_info(store: int) -> is_store_info:
 def is_topk(store: int, q_f16, n_q: int, k: int, ids, scores, stream=None) -> None:
     """q_f16, ids, scores: device tensors (int16/uint16-viewed fp16, int32, float32)."""
     _check(lib().is_topk(store, _dev(q_f16), n_q, k, _dev(ids), _dev(scores), _stream(stream)))
+
+
+def is_retrieve_inject(store: int, q_f16, n_req: int, k: int, prefix_len, block_tables,
+                       cache: is_cache, rope: is_rope, status, ids=None, stream=None) -> None:
+    """q_f16, prefix_len, block_tables ([n_req][max_blocks] int32), status
+    (int32, one element) and the optional ids ([n_req][k] int32) are device
+    tensors; the status is written on the stream."""
+    max_blocks = int(block_tables.shape[1]) if n_req > 0 else 1
+    _check(lib().is_retrieve_inject(store, _dev(q_f16), n_req, k, _dev(prefix_len),
+                                    _dev(block_tables), max_blocks, ctypes.byref(cache),
+                                    ctypes.byref(rope), _dev(ids) if ids is not None else None,
+                                    _dev(status), _stream(stream)))
 
 
 def make_cache(k_base, v_base, strides, block_size, n_blocks, dtype) -> is_cache:

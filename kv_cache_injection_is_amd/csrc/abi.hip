@@ -48,6 +48,9 @@ struct Slot {
 
 constexpr int kSlots = 4;
 constexpr int kTopkSlots = 2;
+// Largest cache (in slots) the on-device overlap check covers: its bitmap
+// takes slots / 8 bytes of scratch.
+constexpr int64_t kDeviceCheckSlots = int64_t(1) << 32;
 
 }  // namespace
 
@@ -74,6 +77,10 @@ struct is_store {
   std::vector<uint64_t> k_addr;   // [n_facts] device-visible block addresses
   std::vector<uint64_t> v_addr;
   uint16_t* emb = nullptr;
+  // Device copies of the per-fact tables, for composition on the device.
+  int32_t* d_len = nullptr;
+  uint64_t* d_k_addr = nullptr;
+  uint64_t* d_v_addr = nullptr;
   std::mutex mu;
   Slot slots[kSlots];              // inject staging (device + pinned host)
   int next_slot = 0;
@@ -132,6 +139,9 @@ void free_store(is_store* s) {
     if (c.v) (void)hipHostFree(c.v);
   }
   if (s->emb) (void)hipFree(s->emb);
+  if (s->d_len) (void)hipFree(s->d_len);
+  if (s->d_k_addr) (void)hipFree(s->d_k_addr);
+  if (s->d_v_addr) (void)hipFree(s->d_v_addr);
   delete s;
 }
 
@@ -265,6 +275,21 @@ IS_EXPORT int is_store_create(const is_store_desc* d, is_store** out) {
     for (int64_t f = c.f0; f < c.f1; ++f) {
       s->k_addr[f] = (uint64_t)(uintptr_t)((char*)kd + s->fact_bytes(c.f0, f));
       s->v_addr[f] = (uint64_t)(uintptr_t)((char*)vd + s->fact_bytes(c.f0, f));
+    }
+  }
+  {
+    const size_t n = (size_t)s->n_facts;
+    if (hipMalloc((void**)&s->d_len, n * 4) != hipSuccess ||
+        hipMalloc((void**)&s->d_k_addr, n * 8) != hipSuccess ||
+        hipMalloc((void**)&s->d_v_addr, n * 8) != hipSuccess) {
+      free_store(s);
+      return fail(IS_ERR_OOM, "device allocation of the fact tables failed");
+    }
+    if (hipMemcpy(s->d_len, s->len.data(), n * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(s->d_k_addr, s->k_addr.data(), n * 8, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(s->d_v_addr, s->v_addr.data(), n * 8, hipMemcpyHostToDevice) != hipSuccess) {
+      free_store(s);
+      return fail(IS_ERR_HIP, "copy of the fact tables failed");
     }
   }
   if (s->emb_dim > 0) {
@@ -499,5 +524,123 @@ IS_EXPORT int is_topk(const is_store* cs, const uint16_t* q, int32_t n_q, int32_
     e = hipEventRecord(sl->done, st);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
+  return IS_OK;
+}
+
+IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t n_req, int32_t k,
+                                 const int32_t* prefix_len, const int32_t* block_tables,
+                                 int32_t max_blocks, const is_cache* cache, const is_rope* rope,
+                                 int32_t* ids_out, int32_t* status, void* stream) {
+  is::clear_error();
+  if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  is_store* s = const_cast<is_store*>(cs);
+  if (s->emb_dim == 0 || s->emb == nullptr)
+    return fail(IS_ERR_UNSUPPORTED, "store has no embedding index");
+  if (n_req < 0) return fail(IS_ERR_INVALID_ARG, "n_req < 0");
+  if (k < 1 || k > s->n_facts) return fail(IS_ERR_INVALID_ARG, "k must be in [1, n_facts]");
+  if (k > 64) return fail(IS_ERR_UNSUPPORTED, "k > 64");
+  if (status == nullptr) return fail(IS_ERR_INVALID_ARG, "null status word");
+  int rc = is::check_cache(s->dtype, cache);
+  if (rc != IS_OK) return rc;
+  rc = is::check_rope(rope);
+  if (rc != IS_OK) return rc;
+  if (n_req > 0 && (q == nullptr || prefix_len == nullptr || block_tables == nullptr))
+    return fail(IS_ERR_INVALID_ARG, "null query, prefix or block-table pointer");
+  if (max_blocks < 1) return fail(IS_ERR_INVALID_ARG, "max_blocks must be >= 1");
+  if (((uintptr_t)q & 15u) != 0) return fail(IS_ERR_ALIGN, "queries must be 16-byte aligned");
+  const int64_t n_slots = cache->n_blocks * (int64_t)cache->block_size;
+  if (n_slots > kDeviceCheckSlots)
+    return fail(IS_ERR_UNSUPPORTED, "cache too large for the on-device slot check");
+  thread_local std::vector<float> g;
+  is::plan_rope(s->d, rope, &g);
+  const int32_t n_pairs = (int32_t)(g.size() / 2);
+  if (n_pairs > is::kComposeMaxPairs) return fail(IS_ERR_UNSUPPORTED, "head_dim too large");
+  DeviceGuard guard(s->device);
+  std::lock_guard<std::mutex> lock(s->mu);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // One scratch slot: top-k scratch (reused by each group of 128 queries),
+  // then ids and scores of all requests, the work list, the rotation speeds
+  // and the slot bitmap.
+  const int32_t nq_group = std::min<int32_t>(128, std::max<int32_t>(n_req, 1));
+  const is::TopkScratch lay = is::topk_scratch(s->n_facts, nq_group, s->emb_dim);
+  const int64_t n_items = (int64_t)n_req * k;
+  const int64_t slot_words = (n_slots + 63) / 64;
+  const size_t off_ids = align256(lay.bytes);
+  const size_t off_scores = off_ids + align256((size_t)n_items * 4);
+  const size_t off_work = off_scores + align256((size_t)n_items * 4);
+  // batches of more than one request are sorted by fact id on the device
+  const bool sort = n_req > 1 && n_items <= is::kComposeSortMax;
+  const size_t off_tmp = off_work + align256((size_t)n_items * sizeof(is::WorkItem));
+  const size_t off_g = off_tmp + (sort ? align256((size_t)n_items * sizeof(is::WorkItem)) : 0);
+  const size_t off_bits = off_g + align256((size_t)n_pairs * 8);
+  const size_t total = off_bits + align256((size_t)slot_words * 8);
+  Slot* sl = nullptr;
+  rc = acquire_topk_slot(s, total, &sl);
+  if (rc != IS_OK) return rc;
+  char* p = static_cast<char*>(sl->dev);
+  int32_t* ids = ids_out ? ids_out : reinterpret_cast<int32_t*>(p + off_ids);
+  float* scores = reinterpret_cast<float*>(p + off_scores);
+  hipError_t e = hipSuccess;
+  for (int32_t q0 = 0; q0 < n_req; q0 += 128) {
+    is::TopkLaunch a{};
+    a.emb = s->emb;
+    a.q = q + (int64_t)q0 * s->emb_dim;
+    a.n_facts = s->n_facts;
+    a.emb_dim = s->emb_dim;
+    a.n_q = std::min<int32_t>(128, n_req - q0);
+    a.k = k;
+    a.q_pad = reinterpret_cast<uint16_t*>(p + lay.q_off);
+    a.gmax = reinterpret_cast<uint32_t*>(p + lay.gmax_off);
+    a.tau = reinterpret_cast<float*>(p + lay.tau_off);
+    a.count = reinterpret_cast<uint32_t*>(p + lay.count_off);
+    a.cand = reinterpret_cast<uint64_t*>(p + lay.cand_off);
+    a.ids = ids + (int64_t)q0 * k;
+    a.scores = scores + (int64_t)q0 * k;
+    if ((e = is::launch_topk(a, st)) != hipSuccess) return hip_fail(e, "top-k launch");
+  }
+  is::ComposeLaunch c{};
+  c.ids = ids;
+  c.prefix = prefix_len;
+  c.bt = block_tables;
+  c.lens = s->d_len;
+  c.k_addr = s->d_k_addr;
+  c.v_addr = s->d_v_addr;
+  c.n_facts = s->n_facts;
+  c.n_hbm = s->n_hbm;
+  c.n_blocks = cache->n_blocks;
+  c.n_req = n_req;
+  c.k = k;
+  c.max_blocks = max_blocks;
+  c.block_size = cache->block_size;
+  c.slot_bits = reinterpret_cast<uint64_t*>(p + off_bits);
+  c.slot_words = slot_words;
+  c.work = reinterpret_cast<is::WorkItem*>(p + off_work);
+  c.work_tmp = sort ? reinterpret_cast<is::WorkItem*>(p + off_tmp) : nullptr;
+  c.g_out = reinterpret_cast<float2*>(p + off_g);
+  c.status = status;
+  c.n_pairs = n_pairs;
+  for (int32_t i = 0; i < n_pairs; ++i) c.g[i] = make_float2(g[2 * i], g[2 * i + 1]);
+  if ((e = is::launch_compose(c, st)) != hipSuccess) return hip_fail(e, "compose launch");
+  is::InjectLaunch a{};
+  a.kc = cache->k_base;
+  a.vc = cache->v_base;
+  a.s_layer = cache->stride_layer;
+  a.s_block = cache->stride_block;
+  a.s_slot = cache->stride_slot;
+  a.s_head = cache->stride_head;
+  a.work = c.work;
+  a.bt = block_tables;
+  a.g = c.g_out;
+  a.n_items = (int32_t)n_items;
+  a.max_blocks = max_blocks;
+  a.block_size = cache->block_size;
+  a.n_layers = s->L;
+  a.n_heads = s->H;
+  a.head_dim = s->d;
+  a.dtype = s->dtype;
+  a.lanes = is::inject_lanes(s->d, s->dtype);
+  a.status = status;
+  if ((e = is::launch_inject(a, st)) != hipSuccess) return hip_fail(e, "inject launch");
+  if ((e = hipEventRecord(sl->done, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return IS_OK;
 }

@@ -1,0 +1,161 @@
+// On-device composition and validation of a retrieve-and-inject batch.
+//
+// Composition follows the "Online phase" of the InferScale explainer pages
+// ("InferScale: GPU-Native KV Injection for Personalized LLM Serving",
+// technical summary): the retrieved facts of a request form one contiguous
+// segment, here laid out in rank order right after the request's prefix.
+// The checks are the host planner's (ids in range, serving positions below
+// 2^24, block table long enough and its entries in range, no cache slot
+// used twice in the call); an error is recorded in a device status word
+// (the smallest code wins, so the result does not depend on timing) and the
+// inject kernel then writes nothing.
+//
+// Kernels: a clear (status and the slot bitmap to zero, rotation speeds
+// to their device buffer); the composer, one wave per request (k <= 64,
+// one selected fact per lane): an inclusive scan of the lengths gives the
+// positions, and each lane marks its share of the request's block runs in
+// the bitmap with 64-bit atomic ORs -- a bit that was already set is a slot
+// used twice; and, for lists of up to 8192 items, a one-workgroup bitonic
+// sort of the list by fact id in LDS (launch order only: the inject grid
+// then walks the store in layout order, as the host path's list does).
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace is {
+namespace {
+
+constexpr int kClearThreads = 256;
+
+__global__ __launch_bounds__(kClearThreads) void compose_clear(ComposeLaunch a) {
+  const int64_t i0 = (int64_t)blockIdx.x * kClearThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kClearThreads;
+  for (int64_t i = i0; i < a.slot_words; i += stride) a.slot_bits[i] = 0;
+  if (i0 < a.n_pairs) a.g_out[i0] = a.g[i0];
+  if (i0 == 0) *a.status = IS_OK;
+}
+
+__device__ __forceinline__ void record(int32_t* status, int32_t code) { atomicMin(status, code); }
+
+// Sets bits [b0, b1] of the bitmap; true if one of them was set already.
+__device__ bool mark(uint64_t* bits, int64_t b0, int64_t b1) {
+  bool clash = false;
+  for (int64_t w = b0 >> 6; w <= (b1 >> 6); ++w) {
+    const int lo = w == (b0 >> 6) ? (int)(b0 & 63) : 0;
+    const int hi = w == (b1 >> 6) ? (int)(b1 & 63) : 63;
+    const uint64_t m = (hi == 63 ? ~0ull : (1ull << (hi + 1)) - 1) & (~0ull << lo);
+    const uint64_t old = atomicOr(reinterpret_cast<unsigned long long*>(bits + w),
+                                  (unsigned long long)m);
+    clash |= (old & m) != 0;
+  }
+  return clash;
+}
+
+__global__ __launch_bounds__(64) void compose(ComposeLaunch a) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const bool mine = lane < a.k;
+  const int32_t f = mine ? a.ids[(int64_t)r * a.k + lane] : 0;
+  const bool id_ok = f >= 0 && (int64_t)f < a.n_facts;
+  if (mine && !id_ok) record(a.status, IS_ERR_FACT_ID);
+  const int64_t len = (mine && id_ok) ? a.lens[f] : 0;
+  // inclusive scan of the lengths across the wave
+  int64_t incl = len;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int lo = __shfl_up((int)(uint32_t)incl, off);
+    const int hi = __shfl_up((int)(uint32_t)(incl >> 32), off);
+    const int64_t o = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+    if (lane >= off) incl += o;
+  }
+  const int lo_t = __shfl((int)(uint32_t)incl, 63);
+  const int hi_t = __shfl((int)(uint32_t)(incl >> 32), 63);
+  const int64_t T = (int64_t)(((uint64_t)(uint32_t)hi_t << 32) | (uint32_t)lo_t);
+  const int64_t P = a.prefix[r];
+  if (P < 0) {
+    if (lane == 0) record(a.status, IS_ERR_INVALID_ARG);
+    return;
+  }
+  if (P + T > ((int64_t)1 << 24)) {
+    if (lane == 0) record(a.status, IS_ERR_INVALID_ARG);
+    return;
+  }
+  if (mine && id_ok) {
+    WorkItem w;
+    w.k = a.k_addr[f];
+    w.v = a.v_addr[f];
+    w.len = (int32_t)len;
+    w.pos = (int32_t)(P + incl - len);
+    w.req = r;
+    w.tier = (int64_t)f >= a.n_hbm ? 1 : 0;
+    (a.work_tmp ? a.work_tmp : a.work)[(int64_t)r * a.k + lane] = w;
+  }
+  if (T == 0) return;
+  const int64_t B = a.block_size;
+  const int64_t b0 = P / B, b1 = (P + T - 1) / B;
+  if (b1 >= a.max_blocks) {
+    if (lane == 0) record(a.status, IS_ERR_BLOCK_TABLE);
+    return;
+  }
+  const int32_t* bt = a.bt + (int64_t)r * a.max_blocks;
+  for (int64_t b = b0 + lane; b <= b1; b += 64) {
+    const int32_t blk = bt[b];
+    if (blk < 0 || (int64_t)blk >= a.n_blocks) {
+      record(a.status, IS_ERR_BLOCK_TABLE);
+      continue;
+    }
+    const int64_t lo = (P > b * B ? P : b * B) - b * B;
+    const int64_t hi = ((P + T) < (b + 1) * B ? (P + T) : (b + 1) * B) - 1 - b * B;
+    if (mark(a.slot_bits, (int64_t)blk * B + lo, (int64_t)blk * B + hi))
+      record(a.status, IS_ERR_SLOT_OVERLAP);
+  }
+}
+
+constexpr int kSortThreads = 1024;
+
+__global__ __launch_bounds__(kSortThreads) void sort_work(ComposeLaunch a) {
+  __shared__ uint64_t key[kComposeSortMax];
+  const int n = a.n_req * a.k;
+  int N = 2;
+  while (N < n) N <<= 1;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < N; i += kSortThreads)
+    key[i] = i < n ? ((uint64_t)(uint32_t)a.ids[i] << 32) | (uint32_t)i : ~0ull;
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < N; i += kSortThreads) {
+        const int p = i ^ j;
+        if (p > i) {
+          const uint64_t x = key[i], y = key[p];
+          if ((x > y) == ((i & k) == 0)) {
+            key[i] = y;
+            key[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < n; i += kSortThreads) a.work[i] = a.work_tmp[(uint32_t)key[i]];
+}
+
+}  // namespace
+
+hipError_t launch_compose(const ComposeLaunch& a, hipStream_t stream) {
+  if (a.k < 1 || a.k > 64 || a.n_pairs > kComposeMaxPairs) return hipErrorInvalidValue;
+  if (a.work_tmp != nullptr && (int64_t)a.n_req * a.k > kComposeSortMax)
+    return hipErrorInvalidValue;
+  int64_t blocks = (a.slot_words + kClearThreads - 1) / kClearThreads;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(compose_clear, dim3((unsigned)blocks), dim3(kClearThreads), 0, stream, a);
+  if (a.n_req > 0) {
+    hipLaunchKernelGGL(compose, dim3((unsigned)a.n_req), dim3(64), 0, stream, a);
+    if (a.work_tmp != nullptr)
+      hipLaunchKernelGGL(sort_work, dim3(1), dim3(kSortThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace is

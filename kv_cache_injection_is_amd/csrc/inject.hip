@@ -175,6 +175,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectLaunch a) {
   __shared__ float2 cs[TC * HALF];
   __shared__ int64_t slot_off[TC];
 
+  if (a.status != nullptr && *a.status != 0) return;   // the call failed validation
   const WorkItem w = a.work[blockIdx.x];
   const int layer = blockIdx.y;
   const int len = w.len;
@@ -264,6 +265,7 @@ __global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
   __shared__ float2 cs[TC * HALF];
   __shared__ int64_t slot_off[TC];
 
+  if (a.status != nullptr && *a.status != 0) return;   // the call failed validation
 #if IS_R16_LAYER_FAST
   const WorkItem w = a.work[blockIdx.y];
   const int l0 = blockIdx.x * G;
@@ -369,10 +371,17 @@ hipError_t launch_es(const InjectLaunch& a, hipStream_t stream) {
   if (IS_R16 && a.lanes == 8) {
     constexpr int G = IS_R16_LAYERS;
     const unsigned n_groups = (unsigned)((a.n_layers + G - 1) / G);
-    const dim3 grid16 = IS_R16_LAYER_FAST ? dim3(n_groups, (unsigned)a.n_items)
-                                          : dim3((unsigned)a.n_items, n_groups);
-    hipLaunchKernelGGL((inject_row16<ES, IS_R16_THREADS, G, IS_R16_ROWS, IS_R16_TC>), grid16,
-                       dim3(IS_R16_THREADS), 0, stream, a);
+    // the item index is grid y: launch at most 65535 items at a time
+    constexpr int32_t kMaxItems = IS_R16_LAYER_FAST ? 65535 : INT32_MAX;
+    for (int32_t i0 = 0; i0 < a.n_items; i0 += kMaxItems) {
+      InjectLaunch part = a;
+      part.work = a.work + i0;
+      part.n_items = a.n_items - i0 < kMaxItems ? a.n_items - i0 : kMaxItems;
+      const dim3 grid16 = IS_R16_LAYER_FAST ? dim3(n_groups, (unsigned)part.n_items)
+                                            : dim3((unsigned)part.n_items, n_groups);
+      hipLaunchKernelGGL((inject_row16<ES, IS_R16_THREADS, G, IS_R16_ROWS, IS_R16_TC>), grid16,
+                         dim3(IS_R16_THREADS), 0, stream, part);
+    }
     return hipGetLastError();
   }
   const dim3 grid((unsigned)a.n_items, (unsigned)a.n_layers);

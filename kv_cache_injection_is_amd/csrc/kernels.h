@@ -24,9 +24,38 @@ struct InjectLaunch {
   int32_t head_dim;
   int32_t dtype;
   int32_t lanes;          // 16-byte chunks per half row
+  const int32_t* status;  // device status word: the kernel writes nothing unless it is 0
+                          // (null: no check)
 };
 
 hipError_t launch_inject(const InjectLaunch& a, hipStream_t stream);
+
+// On-device composition and validation for a batch whose fact ids come
+// from top-k (the ids never visit the host).
+constexpr int kComposeMaxPairs = 256;   // head_dim / 2 of the widest compiled row
+constexpr int kComposeSortMax = 8192;   // work lists up to this size are sorted on the device
+struct ComposeLaunch {
+  const int32_t* ids;       // [n_req][k]
+  const int32_t* prefix;    // [n_req]
+  const int32_t* bt;        // [n_req][max_blocks]
+  const int32_t* lens;      // [n_facts]
+  const uint64_t* k_addr;   // [n_facts] device-visible K block addresses
+  const uint64_t* v_addr;   // [n_facts]
+  int64_t n_facts, n_hbm, n_blocks;
+  int32_t n_req, k, max_blocks, block_size;
+  uint64_t* slot_bits;      // [slot_words] bitmap of the cache's slots (scratch)
+  int64_t slot_words;
+  WorkItem* work;           // [n_req * k] out
+  WorkItem* work_tmp;       // [n_req * k] scratch: when not null (n_req * k <=
+                            // kComposeSortMax), the list is sorted by fact id
+  float2* g_out;            // [n_pairs] out: the rotation speeds, copied from `g`
+  int32_t* status;          // out: IS_OK or an error code
+  int32_t n_pairs;
+  float2 g[kComposeMaxPairs];
+};
+
+// Clears the bitmap and status, then composes and validates every request.
+hipError_t launch_compose(const ComposeLaunch& a, hipStream_t stream);
 
 // Top-k geometry.  The store keeps the embeddings tile-blocked,
 // [tile of 256 facts][64-dim chunk][256 rows][64] fp16, with the width

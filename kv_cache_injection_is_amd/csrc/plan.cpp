@@ -163,16 +163,9 @@ bool runs_overlap(const std::vector<SlotRun>& runs, int64_t B, int64_t n_blocks)
 
 }  // namespace
 
-int plan_inject(const StoreGeom& g, int32_t n_req, const int32_t* req_off,
-                const int32_t* fact_ids, const int32_t* prefix_len,
-                const int32_t* block_tables, int32_t max_blocks,
-                const is_cache* c, const is_rope* rope,
-                std::vector<WorkItem>* items, int64_t* n_tokens) {
-  if (n_req < 0) return fail(IS_ERR_INVALID_ARG, "n_req < 0");
+int check_cache(int32_t dtype, const is_cache* c) {
   if (c == nullptr) return fail(IS_ERR_INVALID_ARG, "null cache");
-  int rc = check_rope(rope);
-  if (rc != IS_OK) return rc;
-  if (c->dtype != g.dtype) return fail(IS_ERR_DTYPE, "cache dtype differs from the store's");
+  if (c->dtype != dtype) return fail(IS_ERR_DTYPE, "cache dtype differs from the store's");
   if (c->block_size < 1 || c->n_blocks < 1)
     return fail(IS_ERR_INVALID_ARG, "cache block_size and n_blocks must be >= 1");
   if (c->n_blocks > INT32_MAX) return fail(IS_ERR_INVALID_ARG, "n_blocks must fit int32");
@@ -180,11 +173,24 @@ int plan_inject(const StoreGeom& g, int32_t n_req, const int32_t* req_off,
     return fail(IS_ERR_INVALID_ARG, "null cache base pointer");
   if (c->stride_layer < 0 || c->stride_block < 0 || c->stride_slot < 0 || c->stride_head < 0)
     return fail(IS_ERR_INVALID_ARG, "negative cache stride");
-  const int es = elem_size(g.dtype);
+  const int es = elem_size(dtype);
   if (!aligned16(c->k_base) || !aligned16(c->v_base) ||
       (c->stride_layer * es) % 16 || (c->stride_block * es) % 16 ||
       (c->stride_slot * es) % 16 || (c->stride_head * es) % 16)
     return fail(IS_ERR_ALIGN, "cache rows must start on 16-byte boundaries");
+  return IS_OK;
+}
+
+int plan_inject(const StoreGeom& g, int32_t n_req, const int32_t* req_off,
+                const int32_t* fact_ids, const int32_t* prefix_len,
+                const int32_t* block_tables, int32_t max_blocks,
+                const is_cache* c, const is_rope* rope,
+                std::vector<WorkItem>* items, int64_t* n_tokens) {
+  if (n_req < 0) return fail(IS_ERR_INVALID_ARG, "n_req < 0");
+  int rc = check_cache(g.dtype, c);
+  if (rc != IS_OK) return rc;
+  rc = check_rope(rope);
+  if (rc != IS_OK) return rc;
   if (n_req == 0) {
     if (items) items->clear();
     if (n_tokens) *n_tokens = 0;

@@ -47,6 +47,10 @@ int check_store_desc(const is_store_desc* d);
 // head_dim / dtype pair is outside the compiled shapes.
 int inject_lanes(int32_t head_dim, int32_t dtype);
 
+// Checks a cache descriptor against the store's dtype (geometry, 16-byte
+// alignment of every row).
+int check_cache(int32_t dtype, const is_cache* cache);
+
 // Validates an inject call and, if `items` is not null, builds its work
 // list.  Returns IS_OK or the first error.
 int plan_inject(const StoreGeom& g, int32_t n_req, const int32_t* req_off,
