@@ -56,7 +56,10 @@ constexpr int kKC = kTopkChunk;       // dims per chunk
 constexpr int kEPieces = kFT * kKC / 8;   // 16-byte pieces of a stage's fact rows
 constexpr int kQPieces = kQB * kKC / 8;   // ... and of its query rows
 constexpr int kEDma = kEPieces / 64 / kWaves;   // DMA instructions per wave per stage
-constexpr int kQDma = kQPieces / 64 / kWaves;
+// Query rows are staged in tiles of 32 (one MFMA column tile); a launch
+// stages and scores only the tiles its queries fill, QT of them.
+template <int QT>
+constexpr int q_dma() { return QT * 32 * kKC / 8 / 64 / kWaves; }   // per wave per stage
 static_assert(kFT == kTopkTile, "tile size");
 
 // Order-preserving map of a float to uint32 (larger float -> larger code).
@@ -143,17 +146,17 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "m
 // against the 128 queries.  k-step s uses logical pieces 2s + grp of every
 // row of both operands (the dot product is order-free in k).  The first
 // chunk of a tile starts from zero accumulators.
-template <bool kFirst>
+template <bool kFirst, int QT>
 __device__ __forceinline__ void mma_chunk(const u32x4* es, const u32x4* qs, int wave, int row,
-                                          int grp, float16v (&acc)[2][4]) {
-  half8 av[2][2], bv[2][4];
+                                          int grp, float16v (&acc)[2][QT]) {
+  half8 av[2][2], bv[2][QT];
   auto load = [&](int s, int buf) {
     const int p = 2 * s + grp;
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
       av[buf][ft] = __builtin_bit_cast(half8, es[piece_slot(wave * kFTW + ft * 32 + row, p)]);
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
       bv[buf][qt] = __builtin_bit_cast(half8, qs[piece_slot(qt * 32 + row, p)]);
   };
   const float16v zero = {};
@@ -164,14 +167,15 @@ __device__ __forceinline__ void mma_chunk(const u32x4* es, const u32x4* qs, int 
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
+      for (int qt = 0; qt < QT; ++qt)
         acc[ft][qt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
             av[s & 1][ft], bv[s & 1][qt], (kFirst && s == 0) ? zero : acc[ft][qt], 0, 0, 0);
   }
 }
 
-template <bool kSample>
+template <bool kSample, int QT>
 __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
+  constexpr int kQDma = q_dma<QT>();
   __shared__ ScanSmem sm;
   const int tid = threadIdx.x;
   const int wave = tid / 64;
@@ -187,9 +191,9 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
   const int total = my_tiles * n_chunks;
   const int64_t edge_tile = (a.n_facts - 1) / kFT;   // the tile that may hold padding rows
 
-  float tau[4];
+  float tau[QT];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int q = qt * 32 + row;
     tau[qt] = (!kSample && q < a.n_q) ? a.tau[q] : 0.f;
   }
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
     if (++qb == kStages) qb = 0;
   };
 
-  float16v acc[2][4];
+  float16v acc[2][QT];
   auto emit = [&](int64_t t) {
     const bool edge = (t == edge_tile);
 #pragma unroll
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
       // element e of a lane's fragment is fact f0 + 8 * (e / 4) + e % 4
       const int64_t f0 = t * kFT + wave * kFTW + ft * 32 + 4 * grp;
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         const int q = qt * 32 + row;
         float v[16];
 #pragma unroll
@@ -301,9 +305,9 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
     ring_barrier();   // every wave's transfers for chunk g landed; chunk g-1's query rows are free
     if (g + 2 < total) issue_q();
     if (cc == 0)
-      mma_chunk<true>(sm.e[cb], sm.q[cb], wave, row, grp, acc);
+      mma_chunk<true, QT>(sm.e[cb], sm.q[cb], wave, row, grp, acc);
     else
-      mma_chunk<false>(sm.e[cb], sm.q[cb], wave, row, grp, acc);
+      mma_chunk<false, QT>(sm.e[cb], sm.q[cb], wave, row, grp, acc);
     if (cc == n_chunks - 1) emit(ct);
     if (++cc == n_chunks) {
       cc = 0;
@@ -552,9 +556,23 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
     a.emb_dim = padded;
   }
   const int sample_wgs = (int)(a.sample_tiles < kTopkMaxScanWG ? a.sample_tiles : kTopkMaxScanWG);
-  hipLaunchKernelGGL((topk_scan<true>), dim3((unsigned)sample_wgs), dim3(kThreads), 0, stream, a);
+  // query tiles of 32 the launch fills: 1, 2 or 4
+  const int qt = a.n_q <= 32 ? 1 : a.n_q <= 64 ? 2 : 4;
+  auto scan = [&](bool sample, unsigned wgs) {
+    const dim3 g(wgs), b(kThreads);
+    if (sample) {
+      if (qt == 1) hipLaunchKernelGGL((topk_scan<true, 1>), g, b, 0, stream, a);
+      else if (qt == 2) hipLaunchKernelGGL((topk_scan<true, 2>), g, b, 0, stream, a);
+      else hipLaunchKernelGGL((topk_scan<true, 4>), g, b, 0, stream, a);
+    } else {
+      if (qt == 1) hipLaunchKernelGGL((topk_scan<false, 1>), g, b, 0, stream, a);
+      else if (qt == 2) hipLaunchKernelGGL((topk_scan<false, 2>), g, b, 0, stream, a);
+      else hipLaunchKernelGGL((topk_scan<false, 4>), g, b, 0, stream, a);
+    }
+  };
+  scan(true, (unsigned)sample_wgs);
   hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
-  hipLaunchKernelGGL((topk_scan<false>), dim3((unsigned)a.scan_wgs), dim3(kThreads), 0, stream, a);
+  scan(false, (unsigned)a.scan_wgs);
   hipLaunchKernelGGL(topk_final, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }

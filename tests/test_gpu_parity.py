@@ -167,6 +167,7 @@ def test_inject_invalid_call_writes_nothing(gpu):
     (1000, 128, 7, 10),      # several tiles, ragged tail
     (5003, 1024, 100, 50),   # 20 workgroups, the 100-query batch
     (3000, 256, 130, 64),    # two query blocks, k at its maximum
+    (2000, 192, 40, 20),     # two 32-query tiles, width not a multiple of 128
     (70000, 128, 3, 1),      # all 256 workgroups, several tiles each
 ])
 def test_topk_parity(gpu, n_facts, dim, n_q, k):
