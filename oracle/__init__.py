@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.or_token_slots.restype = c.c_int64
         L.or_dot.argtypes = [c.c_void_p, c.c_void_p, c.c_int64]
         L.or_dot.restype = c.c_double
+        L.or_attend.argtypes = ([c.c_int] * 5 + [c.c_void_p, c.c_int, c.c_int]
+                                + [c.c_void_p] * 4 + [c.c_int, c.c_int, c.c_int64]
+                                + [c.c_void_p] * 2 + [c.c_int64] * 4 + [c.c_void_p] * 2)
+        L.or_attend.restype = c.c_int
         _lib = L
     return _lib
 
@@ -172,3 +176,25 @@ def inject(n_layers, n_heads, d, dtype, k_store, v_store, tok_off, req_off, fact
                          n_blocks, _p(k_cache), _p(v_cache), *strides, _p(f))
     if rc != 0:
         raise ValueError("oracle inject: index out of range")
+
+
+def attend(n_layers, n_kv_heads, n_q_heads, d, dtype, q, qpos, ctx_begin, ctx_end,
+           block_tables, block_size, n_blocks, k_cache, v_cache, strides, freqs) -> np.ndarray:
+    """Query-only attention over a paged host cache (see or_attend).  q:
+    [n_layers][n_req][n_qtok][n_q_heads][d] raw dtype elements (uint16 bf16
+    bits or float32); returns fp64 of the same shape."""
+    q = np.ascontiguousarray(q)
+    n_req, n_qtok = q.shape[1], q.shape[2]
+    qpos = np.ascontiguousarray(qpos, dtype=np.int32)
+    cb = np.ascontiguousarray(ctx_begin, dtype=np.int32)
+    ce = np.ascontiguousarray(ctx_end, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    f = np.ascontiguousarray(freqs, dtype=np.float64)
+    out = np.zeros(q.shape, dtype=np.float64)
+    rc = lib().or_attend(n_layers, n_kv_heads, n_q_heads, d, dtype, _p(q), n_req, n_qtok,
+                         _p(qpos), _p(cb), _p(ce), _p(bt), bt.shape[1], block_size, n_blocks,
+                         _p(np.ascontiguousarray(k_cache)), _p(np.ascontiguousarray(v_cache)),
+                         *strides, _p(f), _p(out))
+    if rc != 0:
+        raise ValueError("oracle attend: position outside the block table or cache")
+    return out

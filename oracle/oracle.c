@@ -14,7 +14,10 @@
  *   - Online phase, "Injection": the composed K/V are scatter-copied into the
  *     paged KV cache;
  *   - Contributions, "GPU-native system design": retrieval over a
- *     GPU-resident index picks the facts (here: exact inner-product top-k).
+ *     GPU-resident index picks the facts (here: exact inner-product top-k);
+ *   - Online phase, query-only prefill: the engine then runs attention of
+ *     the query over the cache holding the injected facts (here: synthetic
+ *     queries, softmax attention with grouped kv heads, or_attend).
  * The pages give no formulas.  Readings taken here, where the pages are
  * silent: textbook RoPE (Su et al., RoFormer) with frequencies
  * theta^(-2i/d) and rotate-half pairing (i, i + d/2); the published
@@ -311,5 +314,87 @@ EXPORT int or_inject(int n_layers, int n_heads, int d, int dtype,
   }
   free(len);
   free(start);
+  return bad ? -1 : 0;
+}
+
+/* -------------------------------------------------------------- attention */
+
+/*
+ * Query-only attention over a paged host cache: the step that follows the
+ * injection, when the engine prefills only the query over a cache that
+ * already holds the injected facts (Online phase; Theorem 6 says the scores
+ * equal those of a cache prefilled at the same positions).  For layer l,
+ * request r, query token t at position qpos[r] + t and query head hq, whose
+ * kv head is hq / g (g = n_q_heads / n_kv_heads):
+ *   s_p = <R(qpos[r] + t) q, K_l[slot_r(p)][hq / g]> / sqrt(d),
+ *         p in [cb[r], ce[r]),  slot_r(p) = bt[r][p / B] * B + p mod B
+ *   out = sum_p softmax(s)_p V_l[slot_r(p)][hq / g]
+ * q: [n_layers][n_req][n_qtok][n_q_heads][d] in `dtype`, before RoPE; it is
+ * rotated here in fp64.  out: fp64, same shape.  An empty context gives
+ * zeros.  Returns -1 if a position's block lies outside the table or the
+ * cache (nothing is written for that row), else 0.
+ */
+EXPORT int or_attend(int n_layers, int n_kv_heads, int n_q_heads, int d, int dtype,
+                     const void* q, int n_req, int n_qtok, const int32_t* qpos,
+                     const int32_t* cb, const int32_t* ce, const int32_t* block_tables,
+                     int max_blocks, int block_size, int64_t n_blocks, const void* k_cache,
+                     const void* v_cache, int64_t s_layer, int64_t s_block, int64_t s_slot,
+                     int64_t s_head, const double* f, double* out) {
+  const int g = n_q_heads / n_kv_heads;
+  const double scale = 1.0 / sqrt((double)d);
+  int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
+  for (int l = 0; l < n_layers; ++l)
+    for (int r = 0; r < n_req; ++r) {
+      const int64_t n_ctx = ce[r] > cb[r] ? (int64_t)ce[r] - cb[r] : 0;
+      double* x = (double*)malloc(sizeof(double) * (size_t)d);
+      double* qr = (double*)malloc(sizeof(double) * (size_t)d);
+      double* s = (double*)malloc(sizeof(double) * (size_t)(n_ctx > 0 ? n_ctx : 1));
+      int64_t* row = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_ctx > 0 ? n_ctx : 1));
+      /* element offset of each context position's slot (head 0) */
+      for (int64_t j = 0; j < n_ctx; ++j) {
+        const int64_t p = cb[r] + j;
+        const int64_t bi = p / block_size;
+        const int32_t blk = bi < max_blocks ? block_tables[(int64_t)r * max_blocks + bi] : -1;
+        if (blk < 0 || blk >= n_blocks) {
+          bad = 1;
+          row[j] = -1;
+          continue;
+        }
+        row[j] = l * s_layer + blk * s_block + (p % block_size) * s_slot;
+      }
+      for (int t = 0; t < n_qtok; ++t)
+        for (int hq = 0; hq < n_q_heads; ++hq) {
+          const int64_t qi = ((((int64_t)l * n_req + r) * n_qtok + t) * n_q_heads + hq) * d;
+          const int64_t kvh = hq / g;
+          for (int i = 0; i < d; ++i) x[i] = load_elem(q, qi + i, dtype);
+          or_rotate(x, d, (double)qpos[r] + t, f, qr);
+          double mx = -INFINITY;
+          for (int64_t j = 0; j < n_ctx; ++j) {
+            if (row[j] < 0) continue;
+            double acc = 0.0;
+            const int64_t kb = row[j] + kvh * s_head;
+            for (int i = 0; i < d; ++i) acc += qr[i] * load_elem(k_cache, kb + i, dtype);
+            s[j] = acc * scale;
+            if (s[j] > mx) mx = s[j];
+          }
+          double sum = 0.0;
+          for (int64_t j = 0; j < n_ctx; ++j) {
+            if (row[j] < 0) continue;
+            s[j] = exp(s[j] - mx);
+            sum += s[j];
+          }
+          for (int i = 0; i < d; ++i) out[qi + i] = 0.0;
+          for (int64_t j = 0; j < n_ctx; ++j) {
+            if (row[j] < 0) continue;
+            const int64_t vb = row[j] + kvh * s_head;
+            for (int i = 0; i < d; ++i) out[qi + i] += s[j] / sum * load_elem(v_cache, vb + i, dtype);
+          }
+        }
+      free(x);
+      free(qr);
+      free(s);
+      free(row);
+    }
   return bad ? -1 : 0;
 }

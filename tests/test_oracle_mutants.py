@@ -28,6 +28,13 @@ MUTANTS = {
     "half_exponent": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
     "value_source": ("copy_elem(v_cache, dst + i, v_store, src + i, dtype);",
                      "copy_elem(v_cache, dst + i, k_store, src + i, dtype);"),
+    "attend_scale": ("const double scale = 1.0 / sqrt((double)d);",
+                     "const double scale = 1.0 / (double)d;"),
+    "attend_kv_head": ("const int64_t kvh = hq / g;", "const int64_t kvh = hq % n_kv_heads;"),
+    "attend_query_position": ("or_rotate(x, d, (double)qpos[r] + t, f, qr);",
+                              "or_rotate(x, d, (double)qpos[r], f, qr);"),
+    "attend_value_source": ("* load_elem(v_cache, vb + i, dtype);",
+                            "* load_elem(k_cache, vb + i, dtype);"),
 }
 
 

@@ -450,3 +450,139 @@ def test_dot_exact_against_fractions():
     ref = sum(Fraction(float(x)) * Fraction(float(y)) for x, y in
               zip(a.view(np.float16).astype(np.float64), b.view(np.float16).astype(np.float64)))
     assert oracle.dot(a, b) == pytest.approx(float(ref), abs=1e-15)
+
+
+# -------------------------------------------------------------- attention
+# Query-only attention over the paged cache (the step after injection).
+
+def _nhd(L, nb, B, H, d):
+    return (nb * B * H * d, B * H * d, H * d, d)
+
+
+def test_attention_single_position_returns_its_value():
+    L, H, Hq, d, B, nb = 2, 2, 4, 8, 4, 6
+    rng = np.random.default_rng(11)
+    kc = rng.normal(size=(L, nb, B, H, d)).astype(np.float32)
+    vc = rng.normal(size=(L, nb, B, H, d)).astype(np.float32)
+    q = rng.normal(size=(L, 1, 3, Hq, d)).astype(np.float32)
+    bt = np.array([[3, 1, 5]], np.int32)
+    f = oracle.rope_freqs(d, 1e4)
+    out = oracle.attend(L, H, Hq, d, synth.F32, q, [9], [6], [7], bt, B, nb, kc, vc,
+                        _nhd(L, nb, B, H, d), f)
+    for l in range(L):
+        for hq in range(Hq):
+            # position 6: block bt[0][1] = 1, slot 2; kv head hq // 2
+            assert np.array_equal(out[l, 0, :, hq], np.tile(vc[l, 1, 2, hq // 2], (3, 1)))
+
+
+def test_attention_zero_query_averages_values_and_empty_context_is_zero():
+    L, H, Hq, d, B, nb = 1, 1, 2, 16, 4, 8
+    rng = np.random.default_rng(12)
+    kc = rng.normal(size=(L, nb, B, H, d)).astype(np.float32)
+    vc = rng.normal(size=(L, nb, B, H, d)).astype(np.float32)
+    bt = np.array([[7, 2, 4, 0], [1, 3, 5, 6]], np.int32)
+    q = np.zeros((L, 2, 2, Hq, d), np.float32)
+    f = oracle.rope_freqs(d, 1e4)
+    out = oracle.attend(L, H, Hq, d, synth.F32, q, [12, 12], [1, 5], [10, 5], bt, B, nb, kc, vc,
+                        _nhd(L, nb, B, H, d), f)
+    rows = [vc[0, bt[0, p // B], p % B, 0].astype(np.float64) for p in range(1, 10)]
+    assert np.allclose(out[0, 0], np.mean(rows, axis=0), atol=1e-12, rtol=0)
+    assert np.array_equal(out[0, 1], np.zeros((2, Hq, d)))
+
+
+def test_attention_two_positions_logistic_weights():
+    """At position 0 RoPE is the identity; two context keys give weights
+    1 / (1 + exp(s2 - s1)) with s = <q, k> / sqrt(d)."""
+    L, H, Hq, d, B, nb = 1, 1, 1, 32, 8, 2
+    rng = np.random.default_rng(13)
+    kc = np.zeros((L, nb, B, H, d), np.float32)
+    vc = rng.normal(size=(L, nb, B, H, d)).astype(np.float32)
+    q = rng.normal(size=(L, 1, 1, Hq, d)).astype(np.float32)
+    k1 = rng.normal(size=d).astype(np.float32)
+    k2 = rng.normal(size=d).astype(np.float32)
+    bt = np.array([[1, 0]], np.int32)
+    kc[0, 1, 3, 0], kc[0, 1, 4, 0] = k1, k2          # positions 3 and 4
+    f = oracle.rope_freqs(d, 1e4)
+    out = oracle.attend(L, H, Hq, d, synth.F32, q, [0], [3], [5], bt, B, nb, kc, vc,
+                        _nhd(L, nb, B, H, d), f)
+    qq = q[0, 0, 0, 0].astype(np.float64)
+    s1 = float(qq @ k1.astype(np.float64)) / math.sqrt(d)
+    s2 = float(qq @ k2.astype(np.float64)) / math.sqrt(d)
+    w1 = 1.0 / (1.0 + math.exp(s2 - s1))
+    ref = w1 * vc[0, 1, 3, 0].astype(np.float64) + (1 - w1) * vc[0, 1, 4, 0].astype(np.float64)
+    assert np.allclose(out[0, 0, 0, 0], ref, atol=1e-12, rtol=0)
+
+
+def _injected_attention(shift, n_qtok=3, Hq=4):
+    """Injects the small problem's facts (fp32 cache, prefixes + shift) and
+    attends over each request's segment from queries right after it."""
+    P = _small_problem(synth.F32, n_blocks=256)
+    L, H, d, B, nb = P["L"], P["H"], P["d"], P["B"], P["n_blocks"]
+    f = oracle.rope_freqs(d, 1e4)
+    prefix = P["prefix"] + shift
+    T = np.array([P["lens"][P["ids"][P["req_off"][r]:P["req_off"][r + 1]]].sum()
+                  for r in range(3)])
+    need = prefix + T
+    bt = synth.block_tables(4, need, B, nb)
+    kc = np.zeros(L * nb * B * H * d, np.float32)
+    vc = np.zeros_like(kc)
+    oracle.inject(L, H, d, synth.F32, P["K"], P["V"], P["tok_off"], P["req_off"], P["ids"],
+                  prefix, bt, B, nb, kc, vc, _nhd(L, nb, B, H, d), f)
+    q = np.random.default_rng(14).normal(size=(L, 3, n_qtok, Hq, d)).astype(np.float32)
+    qpos = prefix + T + 2
+    out = oracle.attend(L, H, Hq, d, synth.F32, q, qpos, prefix, prefix + T, bt, B, nb, kc, vc,
+                        _nhd(L, nb, B, H, d), f)
+    return P, q, qpos, prefix, out, f
+
+
+def test_attention_over_injected_keys_equals_relative_position_form():
+    """Theorem 6 through attention: with the facts' pre-RoPE keys injected at
+    positions n and the query at m, every score equals <q, R(n - m) k> (RoPE
+    in complex form), so the output is the softmax-weighted sum of the raw
+    values with those scores; kv head of query head hq is hq // g."""
+    P, q, qpos, prefix, out, f = _injected_attention(0)
+    L, H, d = P["L"], P["H"], P["d"]
+    Hq = q.shape[3]
+    g = Hq // H
+    h2 = d // 2
+    for r in range(3):
+        keys, vals, pos = [], [], []
+        n = int(prefix[r])
+        for j in range(P["req_off"][r], P["req_off"][r + 1]):
+            fid = int(P["ids"][j])
+            ln = int(P["lens"][fid])
+            base = int(P["tok_off"][fid]) * L * H * d
+            blk = P["K"][base:base + ln * L * H * d].reshape(L, H, ln, d).astype(np.float64)
+            vbl = P["V"][base:base + ln * L * H * d].reshape(L, H, ln, d).astype(np.float64)
+            for t in range(ln):
+                keys.append(blk[:, :, t])
+                vals.append(vbl[:, :, t])
+                pos.append(n + t)
+            n += ln
+        keys, vals, pos = np.array(keys), np.array(vals), np.array(pos)
+        for l in range(L):
+            for t in range(q.shape[2]):
+                m = int(qpos[r]) + t
+                for hq in range(Hq):
+                    kk = keys[:, l, hq // g]
+                    z = (kk[:, :h2] + 1j * kk[:, h2:]) * np.exp(1j * np.outer(pos - m, f))
+                    rk = np.concatenate([z.real, z.imag], axis=1)
+                    s = rk @ q[l, r, t, hq].astype(np.float64) / math.sqrt(d)
+                    w = np.exp(s - s.max())
+                    ref = (w / w.sum()) @ vals[:, l, hq // g]
+                    assert np.allclose(out[l, r, t, hq], ref, atol=2e-6, rtol=0)
+
+
+def test_attention_invariant_under_shared_shift():
+    _, _, _, _, out0, _ = _injected_attention(0)
+    _, _, _, _, out1, _ = _injected_attention(517)
+    assert np.allclose(out0, out1, atol=2e-6, rtol=0)
+
+
+def test_attention_rejects_positions_outside_the_table():
+    L, H, d, B, nb = 1, 1, 8, 4, 2
+    kc = np.zeros((L, nb, B, H, d), np.float32)
+    q = np.zeros((L, 1, 1, H, d), np.float32)
+    with pytest.raises(ValueError):
+        oracle.attend(L, H, H, d, synth.F32, q, [9], [0], [9], np.array([[0, 1]], np.int32), B,
+                      nb, kc, kc, _nhd(L, nb, B, H, d), oracle.rope_freqs(d, 1e4))
