@@ -245,6 +245,35 @@ int is_retrieve_inject(const is_store* s, const uint16_t* q_f16, int32_t n_req, 
                        int32_t* ids_out, int32_t* status, void* stream);
 
 /*
+ * Query-only attention over the paged cache, the step that follows the
+ * injection (Online phase: the engine prefills only the query over the
+ * cache holding the injected facts; Theorem 6).  For every layer l of the
+ * store's geometry, request r, query token t at position q_pos[r] + t and
+ * query head hq (kv head hq / g, g = n_q_heads / n_kv_heads):
+ *   out = sum_p softmax_p(<R(q_pos[r] + t) q, K_l[slot_r(p)][hq / g]> / sqrt(d))
+ *               * V_l[slot_r(p)][hq / g],  p in [ctx_begin[r], ctx_end[r])
+ * with slot_r(p) = block_tables[r][p / block_size] * block_size
+ * + p % block_size; an empty context gives zeros.
+ *   q     device [n_layers][n_req][n_qtok][n_q_heads][head_dim] bf16 bits,
+ *         before RoPE (rotated here in fp32), 16-byte aligned
+ *   out   device fp32, same shape, 16-byte aligned
+ *   q_pos, ctx_begin, ctx_end   host [n_req]
+ *   block_tables                host [n_req][max_blocks]
+ * Products run on the matrix cores with the fp32 operands (rotated query,
+ * probabilities) split into two bf16 parts; accumulation is fp32.
+ * Validation before any work: positions in [0, 2^24), 0 <= begin <= end,
+ * block tables cover every context position with entries in [0, n_blocks).
+ * Host arrays are copied before return; the kernel runs on `stream`.
+ * Covers bf16 stores with head_dim 128 (else IS_ERR_UNSUPPORTED).
+ * Errors: IS_ERR_INVALID_ARG, IS_ERR_BLOCK_TABLE, IS_ERR_DTYPE, IS_ERR_ALIGN,
+ * IS_ERR_UNSUPPORTED, IS_ERR_OOM, IS_ERR_HIP.
+ */
+int is_attend(const is_store* s, const is_cache* cache, const is_rope* rope, int32_t n_req,
+              int32_t n_qtok, int32_t n_q_heads, const uint16_t* q, const int32_t* q_pos,
+              const int32_t* ctx_begin, const int32_t* ctx_end, const int32_t* block_tables,
+              int32_t max_blocks, float* out, void* stream);
+
+/*
  * The host half of is_inject on its own: validation and composition
  * against a store description (no store, no GPU).  Returns the status
  * is_inject would return for the same arguments before any device work,

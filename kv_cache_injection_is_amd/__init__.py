@@ -25,7 +25,8 @@ IS_DTYPE_F32, IS_DTYPE_BF16 = 0, 1
 IS_ROPE_NONE, IS_ROPE_LLAMA3 = 0, 1
 
 EXPORTS = ("is_store_create", "is_store_load", "is_store_get_info", "is_topk", "is_inject",
-           "is_retrieve_inject", "is_inject_check", "is_store_destroy", "is_last_error")
+           "is_retrieve_inject", "is_attend", "is_inject_check", "is_store_destroy",
+           "is_last_error")
 
 
 class ISError(RuntimeError):
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
                                 c.POINTER(is_rope), P]
         L.is_retrieve_inject.argtypes = [P, P, c.c_int32, c.c_int32, P, P, c.c_int32,
                                          c.POINTER(is_cache), c.POINTER(is_rope), P, P, P]
+        L.is_attend.argtypes = [P, c.POINTER(is_cache), c.POINTER(is_rope), c.c_int32,
+                                c.c_int32, c.c_int32, P, P, P, P, P, c.c_int32, P, P]
         L.is_inject_check.argtypes = [c.POINTER(is_store_desc), c.c_int32, P, P, P, P,
                                       c.c_int32, c.POINTER(is_cache), c.POINTER(is_rope),
                                       c.POINTER(c.c_int64)]
@@ -185,6 +188,20 @@ def is_retrieve_inject(store: int, q_f16, n_req: int, k: int, prefix_len, block_
                                     _dev(block_tables), max_blocks, ctypes.byref(cache),
                                     ctypes.byref(rope), _dev(ids) if ids is not None else None,
                                     _dev(status), _stream(stream)))
+
+
+def is_attend(store: int, cache: is_cache, rope: is_rope, q, n_qtok: int, n_q_heads: int,
+              q_pos, ctx_begin, ctx_end, block_tables, out, stream=None) -> None:
+    """q, out: device tensors [n_layers][n_req][n_qtok][n_q_heads][head_dim]
+    (bf16 bits as int16/uint16, float32); q_pos, ctx_begin, ctx_end ([n_req])
+    and block_tables ([n_req][max_blocks]) are host arrays."""
+    qp, qp_p = _host(q_pos, np.int32)
+    cb, cb_p = _host(ctx_begin, np.int32)
+    ce, ce_p = _host(ctx_end, np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    _check(lib().is_attend(store, ctypes.byref(cache), ctypes.byref(rope), len(qp), n_qtok,
+                           n_q_heads, _dev(q), qp_p, cb_p, ce_p, bt.ctypes.data, bt.shape[1],
+                           _dev(out), _stream(stream)))
 
 
 def make_cache(k_base, v_base, strides, block_size, n_blocks, dtype) -> is_cache:

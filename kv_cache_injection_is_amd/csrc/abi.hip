@@ -644,3 +644,97 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   if ((e = hipEventRecord(sl->done, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return IS_OK;
 }
+
+IS_EXPORT int is_attend(const is_store* cs, const is_cache* cache, const is_rope* rope,
+                        int32_t n_req, int32_t n_qtok, int32_t n_q_heads, const uint16_t* q,
+                        const int32_t* q_pos, const int32_t* ctx_begin, const int32_t* ctx_end,
+                        const int32_t* block_tables, int32_t max_blocks, float* out,
+                        void* stream) {
+  is::clear_error();
+  if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  is_store* s = const_cast<is_store*>(cs);
+  if (s->dtype != IS_DTYPE_BF16 || s->d != 128)
+    return fail(IS_ERR_UNSUPPORTED, "attention covers bf16 caches with head_dim 128");
+  int rc = is::check_cache(s->dtype, cache);
+  if (rc != IS_OK) return rc;
+  rc = is::check_rope(rope);
+  if (rc != IS_OK) return rc;
+  if (n_req < 0 || n_qtok < 0) return fail(IS_ERR_INVALID_ARG, "negative n_req or n_qtok");
+  if (n_q_heads < 1 || n_q_heads % s->H != 0)
+    return fail(IS_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  if ((int64_t)n_qtok * (n_q_heads / s->H) > (1 << 20))
+    return fail(IS_ERR_UNSUPPORTED, "too many query rows per kv head");
+  if (n_req == 0 || n_qtok == 0) return IS_OK;
+  if (q == nullptr || out == nullptr || q_pos == nullptr || ctx_begin == nullptr ||
+      ctx_end == nullptr || block_tables == nullptr)
+    return fail(IS_ERR_INVALID_ARG, "null pointer argument");
+  if (((uintptr_t)q & 15u) != 0 || ((uintptr_t)out & 15u) != 0)
+    return fail(IS_ERR_ALIGN, "q and out must be 16-byte aligned");
+  if (max_blocks < 1) return fail(IS_ERR_INVALID_ARG, "max_blocks must be >= 1");
+  const int64_t B = cache->block_size;
+  for (int32_t r = 0; r < n_req; ++r) {
+    if (q_pos[r] < 0 || (int64_t)q_pos[r] + n_qtok > ((int64_t)1 << 24))
+      return fail(IS_ERR_INVALID_ARG, "query positions must lie in [0, 2^24)");
+    if (ctx_begin[r] < 0 || ctx_end[r] < ctx_begin[r])
+      return fail(IS_ERR_INVALID_ARG, "context range must satisfy 0 <= begin <= end");
+    if (ctx_end[r] == ctx_begin[r]) continue;
+    const int64_t b0 = ctx_begin[r] / B, b1 = ((int64_t)ctx_end[r] - 1) / B;
+    if (b1 >= max_blocks)
+      return fail(IS_ERR_BLOCK_TABLE, "block table of request " + std::to_string(r) +
+                                          " is too short for its context");
+    for (int64_t b = b0; b <= b1; ++b) {
+      const int32_t blk = block_tables[(int64_t)r * max_blocks + b];
+      if (blk < 0 || blk >= cache->n_blocks)
+        return fail(IS_ERR_BLOCK_TABLE, "block table entry " + std::to_string(b) +
+                                            " of request " + std::to_string(r) +
+                                            " is outside [0, n_blocks)");
+    }
+  }
+  thread_local std::vector<float> g;
+  is::plan_rope(s->d, rope, &g);
+  const size_t meta_bytes = align256((size_t)n_req * 3 * sizeof(int32_t));
+  const size_t bt_bytes = align256((size_t)n_req * max_blocks * sizeof(int32_t));
+  const size_t total = meta_bytes + bt_bytes + align256(g.size() * sizeof(float));
+  DeviceGuard guard(s->device);
+  std::lock_guard<std::mutex> lock(s->mu);
+  Slot* sl = nullptr;
+  rc = acquire_slot(s, total, &sl);
+  if (rc != IS_OK) return rc;
+  char* h = static_cast<char*>(sl->host);
+  int32_t* meta = reinterpret_cast<int32_t*>(h);
+  for (int32_t r = 0; r < n_req; ++r) {
+    meta[3 * r] = q_pos[r];
+    meta[3 * r + 1] = ctx_begin[r];
+    meta[3 * r + 2] = ctx_end[r];
+  }
+  std::memcpy(h + meta_bytes, block_tables, (size_t)n_req * max_blocks * sizeof(int32_t));
+  std::memcpy(h + meta_bytes + bt_bytes, g.data(), g.size() * sizeof(float));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(sl->dev, sl->host, total, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "staging copy");
+  const char* dv = static_cast<const char*>(sl->dev);
+  is::AttendLaunch a{};
+  a.kc = cache->k_base;
+  a.vc = cache->v_base;
+  a.s_layer = cache->stride_layer;
+  a.s_block = cache->stride_block;
+  a.s_slot = cache->stride_slot;
+  a.s_head = cache->stride_head;
+  a.q = q;
+  a.out = out;
+  a.meta = reinterpret_cast<const int32_t*>(dv);
+  a.bt = reinterpret_cast<const int32_t*>(dv + meta_bytes);
+  a.g = reinterpret_cast<const float2*>(dv + meta_bytes + bt_bytes);
+  a.n_layers = s->L;
+  a.n_req = n_req;
+  a.n_qtok = n_qtok;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = s->H;
+  a.max_blocks = max_blocks;
+  a.block_size = cache->block_size;
+  a.rows = n_qtok * (n_q_heads / s->H);
+  a.n_units = (int64_t)s->L * n_req * s->H;
+  if ((e = is::launch_attend(a, st)) != hipSuccess) return hip_fail(e, "attention launch");
+  if ((e = hipEventRecord(sl->done, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return IS_OK;
+}

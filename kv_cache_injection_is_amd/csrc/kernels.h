@@ -57,6 +57,24 @@ struct ComposeLaunch {
 // Clears the bitmap and status, then composes and validates every request.
 hipError_t launch_compose(const ComposeLaunch& a, hipStream_t stream);
 
+// Query-only attention over the paged cache (bf16, head_dim 128).
+struct AttendLaunch {
+  const void* kc;           // cache bases
+  const void* vc;
+  int64_t s_layer, s_block, s_slot, s_head;   // cache strides (elements)
+  const uint16_t* q;        // [n_layers][n_req][n_qtok][n_q_heads][128] bf16, before RoPE
+  float* out;               // same shape, fp32
+  const int32_t* meta;      // [n_req][3]: position of query token 0, context begin, end
+  const int32_t* bt;        // [n_req][max_blocks]
+  const float2* g;          // [64] (hi, lo) turns per position
+  int64_t n_units;          // n_layers * n_req * n_kv_heads
+  int32_t n_layers, n_req, n_qtok, n_q_heads, n_kv_heads, max_blocks, block_size;
+  int32_t rows;             // n_qtok * (n_q_heads / n_kv_heads)
+  int32_t groups;           // derived by launch_attend
+};
+
+hipError_t launch_attend(const AttendLaunch& a, hipStream_t stream);
+
 // Top-k geometry.  The store keeps the embeddings tile-blocked,
 // [tile of 256 facts][64-dim chunk][256 rows][64] fp16, with the width
 // padded to a multiple of 64 and rows past n_facts zero, so that every

@@ -35,6 +35,8 @@ def test_null_arguments_are_rejected_without_gpu():
     assert lib.is_inject(None, 0, None, None, None, None, 1, None, None, None) == -1
     assert lib.is_retrieve_inject(None, None, 1, 1, None, None, 1, None, None, None, None,
                                   None) == -1
+    assert lib.is_attend(None, None, None, 1, 1, 1, None, None, None, None, None, 1, None,
+                         None) == -1
 
 
 def _desc(dtype=K.IS_DTYPE_BF16, head_dim=128, lens=(5, 7, 3, 9), emb_dim=0):
