@@ -168,6 +168,48 @@ def device_path(torch, K, st, w, q, stream, cdesc, rope, prefix, bt, tokens, rep
                     "device; median wall time per call including the final synchronize"}
 
 
+def attend_rate(torch, K, synth, st, w, cdesc, rope, prefix, seg_tokens, bt, stream,
+                reps: int) -> dict:
+    """is_attend over the injected batch: 16 query tokens per request, 32
+    query heads (4 per kv head), attending over each request's injected
+    segment in every layer; HIP-event time of back-to-back calls."""
+    n_qtok, n_q_heads = 16, 32
+    n = w.n_layers * w.n_req * n_qtok * n_q_heads * w.head_dim
+    q = torch.empty(n, dtype=torch.int16, device="cuda")
+    off = torch.tensor([0, n], dtype=torch.int64, device="cuda")
+    synth.gpu_fill_kv(w.seed, synth.TAG_K, 4_000_000, off, n, synth.BF16, q.data_ptr(),
+                      stream.cuda_stream)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    cb = prefix.astype(np.int32)
+    ce = (prefix + seg_tokens).astype(np.int32)
+
+    def call():
+        K.is_attend(st.handle, cdesc, rope, q, n_qtok, n_q_heads, ce, cb, ce, bt, out, stream)
+
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    assert bool(torch.isfinite(out).all()), "attention produced non-finite values"
+    tokens = int(seg_tokens.sum())
+    kv_bytes = 2 * tokens * w.token_bytes
+    io_bytes = n * 2 + n * 4
+    gbps = (kv_bytes + io_bytes) / (ms / 1e3) / 1e9
+    g = n_q_heads // w.n_kv_heads
+    flops = 4.0 * w.head_dim * n_qtok * g * w.n_kv_heads * w.n_layers * tokens
+    return {"workload": f"{w.n_req} requests x {n_qtok} query tokens x {n_q_heads} heads over "
+                        f"their injected segments ({tokens} tokens), {w.n_layers} layers",
+            "ms": round(ms, 4), "GBps": round(gbps, 1),
+            "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": kv_bytes + io_bytes,
+            "TFLOPs": round(flops / (ms / 1e3) / 1e12, 2)}
+
+
 def copy_bandwidth(torch, gib: float = 4.0, reps: int = 5) -> float:
     """Plain device copy (read + write) in GB/s."""
     n = int(gib * (1 << 30))
@@ -265,6 +307,7 @@ def main() -> int:
         return 0
 
     import kv_cache_injection_is_amd as K
+    import synth
     from synth import workloads as W
     from tests import harness as Hn
 
@@ -368,6 +411,11 @@ def main() -> int:
         f"{dev['latency_one_request']['k50']['device_path_ms']:.3f} ms "
         f"(host path {dev['latency_one_request']['k50']['host_path_ms']:.3f})")
 
+    seg = np.array([int(st.lens[flat0[req_off[r]:req_off[r + 1]]].sum()) for r in range(n_q)])
+    attend = attend_rate(torch, K, synth, st, w, cdesc, rope, prefix, seg, bt, stream,
+                         max(args.steps, 5))
+    log(f"attention over the injected batch: {attend['ms']:.3f} ms ({attend['GBps']:.0f} GB/s)")
+
     copy_gbps = copy_bandwidth(torch)
     traffic = traffic_from_counters(inj_bytes)
 
@@ -431,6 +479,7 @@ def main() -> int:
                          "each call"},
         "topk_1m": topk_1m,
         "device_path": dev,
+        "attend": attend,
         "copy_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
     }

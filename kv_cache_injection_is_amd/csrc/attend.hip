@@ -10,8 +10,8 @@
 //   over positions p in [ctx_begin_r, ctx_end_r), g = n_q_heads / n_kv_heads.
 //
 // Design (gfx950; bf16 cache, head_dim 128).  One workgroup of four waves
-// per (layer, request, kv head) and group of up to QT * 32 query rows (a row
-// is a (query token, query head of the group) pair).  The waves take the
+// per (layer, request, kv head) and tile of 32 query rows (a row is a
+// (query token, query head of the group) pair).  The waves take the
 // context's 32-token chunks round-robin and merge their softmax states
 // through LDS at the end.  Per chunk a wave forms S^T = K Q^T and
 // O^T += V^T P^T with v_mfma_f32_32x32x16_bf16; in both products the query
@@ -23,9 +23,10 @@
 // on both, so the operands keep 16 bits beyond bf16; accumulation is fp32.
 // K rows go from the cache into MFMA registers directly (each 256-byte row
 // by two lanes, 16 bytes per k-step); V rows are staged in LDS, to be read
-// transposed.  Workgroups of one (layer, request, kv head) that split its
-// query rows run on the same XCD (ids congruent mod 8), so the second reads
-// its K and V from that XCD's L2.
+// transposed; the next chunk's K and V are loaded while the current one is
+// computed.  Workgroups of one (layer, request, kv head) that split its
+// query rows run on the same XCD (ids congruent mod 8) one after another,
+// so all but the first read its K and V from that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -140,7 +141,12 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
         for (int e = 0; e < 8; ++e) x[s][e] = 0.f;
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) split8(x[s], qhi[qt][s], qlo[qt][s]);
+    for (int s = 0; s < 8; ++s) {
+      split8(x[s], qhi[qt][s], qlo[qt][s]);
+      // keep the split in registers: left to itself the compiler recomputes
+      // it from x inside the chunk loop
+      asm volatile("" : "+v"(qhi[qt][s]), "+v"(qlo[qt][s]));
+    }
   }
 
   float m[QT], lsum[QT];
@@ -158,22 +164,40 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
   const int32_t* bt = a.bt + (int64_t)r * a.max_blocks;
   unsigned short* vs = sm.v[wave];
   const int n_ctx = ce - cb;
-  for (int c0 = wave * kChunk; c0 < n_ctx; c0 += kWaves * kChunk) {
-    // this lane's token (positions past the context re-read the first one;
-    // their scores are masked)
+  // Element offset of this lane's K/V row in the chunk starting at c0
+  // (positions past the context re-read the first one; their scores are
+  // masked).
+  auto row_of = [&](int c0) -> int64_t {
     const int tok = c0 + col;
     const int p = cb + (tok < n_ctx ? tok : 0);
-    const int64_t rowe = (int64_t)layer * a.s_layer + (int64_t)bt[p / a.block_size] * a.s_block +
-                         (int64_t)(p % a.block_size) * a.s_slot + (int64_t)kvh * a.s_head;
-    bf16x8 kf[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kc + (rowe + 16 * s + 8 * h) * 2));
+    return (int64_t)layer * a.s_layer + (int64_t)bt[p / a.block_size] * a.s_block +
+           (int64_t)(p % a.block_size) * a.s_slot + (int64_t)kvh * a.s_head;
+  };
+  // The next chunk's K fragments and V rows are loaded into registers while
+  // the current one is computed.
+  bf16x8 kf[8];
+  u32x4 vr[8];
+  auto load_chunk = [&](int64_t rowe) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(vc + (rowe + 16 * s + 8 * h) * 2);
-      *reinterpret_cast<u32x4*>(vs + col * kVPitch + 16 * s + 8 * h) = v;
+      kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kc + (rowe + 16 * s + 8 * h) * 2));
+      vr[s] = *reinterpret_cast<const u32x4*>(vc + (rowe + 16 * s + 8 * h) * 2);
     }
+  };
+  // With two row tiles the registers hold no second chunk: each chunk is
+  // loaded at the top of its own step.
+  constexpr bool kPrefetch = QT == 1;
+  if (kPrefetch && wave * kChunk < n_ctx) load_chunk(row_of(wave * kChunk));
+  for (int c0 = wave * kChunk; c0 < n_ctx; c0 += kWaves * kChunk) {
+    if (!kPrefetch) load_chunk(row_of(c0));
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      *reinterpret_cast<u32x4*>(vs + col * kVPitch + 16 * s + 8 * h) = vr[s];
+    bf16x8 kuse[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kuse[s] = kf[s];
+    const int c1 = c0 + kWaves * kChunk;
+    if (kPrefetch && c1 < n_ctx) load_chunk(row_of(c1));
     // S^T for each row tile: element (token, row) at lane col = row,
     // reg i -> token 8 (i / 4) + 4 h + i % 4
     float16v st[QT];
@@ -182,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
       st[qt] = float16v{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        st[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qhi[qt][s], st[qt], 0, 0, 0);
-        st[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qlo[qt][s], st[qt], 0, 0, 0);
+        st[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kuse[s], qhi[qt][s], st[qt], 0, 0, 0);
+        st[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kuse[s], qlo[qt][s], st[qt], 0, 0, 0);
       }
     }
     // online softmax (base 2); P split for the second product
@@ -192,27 +216,36 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
     for (int qt = 0; qt < QT; ++qt) {
       float sv[16];
       float mx = -INFINITY;
+      const bool tail = c0 + kChunk > n_ctx;   // the last, partial chunk
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int ti = c0 + 8 * (i / 4) + 4 * h + (i % 4);
-        sv[i] = ti < n_ctx ? st[qt][i] : -INFINITY;
+        sv[i] = (!tail || ti < n_ctx) ? st[qt][i] : -INFINITY;
         mx = fmaxf(mx, sv[i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[qt], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
-      m[qt] = mn;
+      // Lazy rescaling: the reference m only moves when some row's maximum
+      // passes it by more than 8 (a factor 256 in the weights); until then
+      // the weights exp2(s - m) may exceed 1 by up to that factor, which the
+      // split operands and fp32 sums carry without loss.
+      if (__builtin_amdgcn_ballot_w64(mx > m[qt] + 8.0f)) {
+        const float mn = fmaxf(m[qt], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
+        m[qt] = mn;
+        lsum[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[qt][dt][i] *= alpha;
+      }
+      const float mn = m[qt];
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         sv[i] = __builtin_amdgcn_exp2f(sv[i] - mn);
         ps += sv[i];
       }
-      lsum[qt] = lsum[qt] * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[qt][dt][i] *= alpha;
+      lsum[qt] += ps;
       split8(sv, phi[qt][0], plo[qt][0]);
       split8(sv + 8, phi[qt][1], plo[qt][1]);
     }
@@ -283,7 +316,12 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
 hipError_t launch_attend(const AttendLaunch& in, hipStream_t stream) {
   if (in.n_units == 0 || in.rows == 0) return hipSuccess;
   AttendLaunch a = in;
-  const int qt = a.rows <= 32 ? 1 : 2;
+  // one 32-row tile per workgroup: with the next chunk double-buffered in
+  // registers, two tiles would not fit the register file
+#ifndef IS_ATTEND_QT
+#define IS_ATTEND_QT 2
+#endif
+  const int qt = a.rows <= 32 ? 1 : IS_ATTEND_QT;
   a.groups = (a.rows + qt * 32 - 1) / (qt * 32);
   const int64_t wgs = (a.n_units + 7) / 8 * 8 * a.groups;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
