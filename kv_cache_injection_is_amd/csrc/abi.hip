@@ -568,10 +568,11 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   const size_t off_ids = align256(lay.bytes);
   const size_t off_scores = off_ids + align256((size_t)n_items * 4);
   const size_t off_work = off_scores + align256((size_t)n_items * 4);
-  // batches of more than one request are sorted by fact id on the device
-  const bool sort = n_req > 1 && n_items <= is::kComposeSortMax;
+  // batches of more than one request are grouped by fact id on the device
+  const bool sort = n_req > 1;
   const size_t off_tmp = off_work + align256((size_t)n_items * sizeof(is::WorkItem));
-  const size_t off_g = off_tmp + (sort ? align256((size_t)n_items * sizeof(is::WorkItem)) : 0);
+  const size_t off_buckets = off_tmp + (sort ? align256((size_t)n_items * sizeof(is::WorkItem)) : 0);
+  const size_t off_g = off_buckets + (sort ? align256(2 * is::kComposeBuckets * sizeof(uint32_t)) : 0);
   const size_t off_bits = off_g + align256((size_t)n_pairs * 8);
   const size_t total = off_bits + align256((size_t)slot_words * 8);
   Slot* sl = nullptr;
@@ -616,6 +617,7 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   c.slot_words = slot_words;
   c.work = reinterpret_cast<is::WorkItem*>(p + off_work);
   c.work_tmp = sort ? reinterpret_cast<is::WorkItem*>(p + off_tmp) : nullptr;
+  c.buckets = sort ? reinterpret_cast<uint32_t*>(p + off_buckets) : nullptr;
   c.g_out = reinterpret_cast<float2*>(p + off_g);
   c.status = status;
   c.n_pairs = n_pairs;

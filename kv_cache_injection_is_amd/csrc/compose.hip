@@ -15,9 +15,11 @@
 // one selected fact per lane): an inclusive scan of the lengths gives the
 // positions, and each lane marks its share of the request's block runs in
 // the bitmap with 64-bit atomic ORs -- a bit that was already set is a slot
-// used twice; and, for lists of up to 8192 items, a one-workgroup bitonic
-// sort of the list by fact id in LDS (launch order only: the inject grid
-// then walks the store in layout order, as the host path's list does).
+// used twice; and, for batches, a counting sort of the list into 4096
+// consecutive fact-id ranges (launch order only: the inject grid then walks
+// the store front to back, as the host path's sorted list does; the order
+// inside a range is whatever the atomics give, which changes no result,
+// since every item writes its own slots).
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -31,11 +33,17 @@ __global__ __launch_bounds__(kClearThreads) void compose_clear(ComposeLaunch a) 
   const int64_t i0 = (int64_t)blockIdx.x * kClearThreads + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kClearThreads;
   for (int64_t i = i0; i < a.slot_words; i += stride) a.slot_bits[i] = 0;
+  if (a.work_tmp != nullptr)
+    for (int64_t i = i0; i < 2 * kComposeBuckets; i += stride) a.buckets[i] = 0;
   if (i0 < a.n_pairs) a.g_out[i0] = a.g[i0];
   if (i0 == 0) *a.status = IS_OK;
 }
 
 __device__ __forceinline__ void record(int32_t* status, int32_t code) { atomicMin(status, code); }
+
+__device__ __forceinline__ int bucket_of(int32_t f, int64_t n_facts) {
+  return (int)((int64_t)f * kComposeBuckets / n_facts);
+}
 
 // Sets bits [b0, b1] of the bitmap; true if one of them was set already.
 __device__ bool mark(uint64_t* bits, int64_t b0, int64_t b1) {
@@ -58,6 +66,7 @@ __global__ __launch_bounds__(64) void compose(ComposeLaunch a) {
   const int32_t f = mine ? a.ids[(int64_t)r * a.k + lane] : 0;
   const bool id_ok = f >= 0 && (int64_t)f < a.n_facts;
   if (mine && !id_ok) record(a.status, IS_ERR_FACT_ID);
+  if (mine && id_ok && a.work_tmp != nullptr) atomicAdd(&a.buckets[bucket_of(f, a.n_facts)], 1u);
   const int64_t len = (mine && id_ok) ? a.lens[f] : 0;
   // inclusive scan of the lengths across the wave
   int64_t incl = len;
@@ -111,49 +120,62 @@ __global__ __launch_bounds__(64) void compose(ComposeLaunch a) {
   }
 }
 
-constexpr int kSortThreads = 1024;
+constexpr int kScanThreads = 1024;
 
-__global__ __launch_bounds__(kSortThreads) void sort_work(ComposeLaunch a) {
-  __shared__ uint64_t key[kComposeSortMax];
-  const int n = a.n_req * a.k;
-  int N = 2;
-  while (N < n) N <<= 1;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < N; i += kSortThreads)
-    key[i] = i < n ? ((uint64_t)(uint32_t)a.ids[i] << 32) | (uint32_t)i : ~0ull;
-  __syncthreads();
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < N; i += kSortThreads) {
-        const int p = i ^ j;
-        if (p > i) {
-          const uint64_t x = key[i], y = key[p];
-          if ((x > y) == ((i & k) == 0)) {
-            key[i] = y;
-            key[p] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
+// Exclusive scan of the bucket counts into the scatter cursors.
+__global__ __launch_bounds__(kScanThreads) void bucket_scan(ComposeLaunch a) {
+  constexpr int kPer = kComposeBuckets / kScanThreads;
+  __shared__ uint32_t wsum[kScanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t c[kPer], sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = a.buckets[tid * kPer + j];
+    sum += c[j];
   }
-  for (int i = tid; i < n; i += kSortThreads) a.work[i] = a.work_tmp[(uint32_t)key[i]];
+  uint32_t incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t base = incl - sum;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    a.buckets[kComposeBuckets + tid * kPer + j] = base;
+    base += c[j];
+  }
+}
+
+// Moves every item with a valid id to the next slot of its bucket.
+__global__ __launch_bounds__(256) void bucket_scatter(ComposeLaunch a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.n_req * a.k) return;
+  const int32_t f = a.ids[i];
+  if (f < 0 || (int64_t)f >= a.n_facts) return;
+  const uint32_t slot = atomicAdd(&a.buckets[kComposeBuckets + bucket_of(f, a.n_facts)], 1u);
+  a.work[slot] = a.work_tmp[i];
 }
 
 }  // namespace
 
 hipError_t launch_compose(const ComposeLaunch& a, hipStream_t stream) {
   if (a.k < 1 || a.k > 64 || a.n_pairs > kComposeMaxPairs) return hipErrorInvalidValue;
-  if (a.work_tmp != nullptr && (int64_t)a.n_req * a.k > kComposeSortMax)
-    return hipErrorInvalidValue;
   int64_t blocks = (a.slot_words + kClearThreads - 1) / kClearThreads;
   if (blocks < 1) blocks = 1;
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(compose_clear, dim3((unsigned)blocks), dim3(kClearThreads), 0, stream, a);
   if (a.n_req > 0) {
     hipLaunchKernelGGL(compose, dim3((unsigned)a.n_req), dim3(64), 0, stream, a);
-    if (a.work_tmp != nullptr)
-      hipLaunchKernelGGL(sort_work, dim3(1), dim3(kSortThreads), 0, stream, a);
+    if (a.work_tmp != nullptr) {
+      const int64_t n = (int64_t)a.n_req * a.k;
+      hipLaunchKernelGGL(bucket_scan, dim3(1), dim3(kScanThreads), 0, stream, a);
+      hipLaunchKernelGGL(bucket_scatter, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                         a);
+    }
   }
   return hipGetLastError();
 }

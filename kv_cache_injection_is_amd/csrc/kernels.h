@@ -33,7 +33,7 @@ hipError_t launch_inject(const InjectLaunch& a, hipStream_t stream);
 // On-device composition and validation for a batch whose fact ids come
 // from top-k (the ids never visit the host).
 constexpr int kComposeMaxPairs = 256;   // head_dim / 2 of the widest compiled row
-constexpr int kComposeSortMax = 8192;   // work lists up to this size are sorted on the device
+constexpr int kComposeBuckets = 4096;   // fact-id ranges the work list is grouped by
 struct ComposeLaunch {
   const int32_t* ids;       // [n_req][k]
   const int32_t* prefix;    // [n_req]
@@ -46,8 +46,9 @@ struct ComposeLaunch {
   uint64_t* slot_bits;      // [slot_words] bitmap of the cache's slots (scratch)
   int64_t slot_words;
   WorkItem* work;           // [n_req * k] out
-  WorkItem* work_tmp;       // [n_req * k] scratch: when not null (n_req * k <=
-                            // kComposeSortMax), the list is sorted by fact id
+  WorkItem* work_tmp;       // [n_req * k] scratch: when not null, the list is
+                            // grouped by fact id (kComposeBuckets ranges)
+  uint32_t* buckets;        // [2 * kComposeBuckets] scratch for the grouping
   float2* g_out;            // [n_pairs] out: the rotation speeds, copied from `g`
   int32_t* status;          // out: IS_OK or an error code
   int32_t n_pairs;
