@@ -10,24 +10,27 @@
 //   over positions p in [ctx_begin_r, ctx_end_r), g = n_q_heads / n_kv_heads.
 //
 // Design (gfx950; bf16 cache, head_dim 128).  One workgroup of four waves
-// per (layer, request, kv head) and tile of 32 query rows (a row is a
-// (query token, query head of the group) pair).  The waves take the
-// context's 32-token chunks round-robin and merge their softmax states
-// through LDS at the end.  Per chunk a wave forms S^T = K Q^T and
-// O^T += V^T P^T with v_mfma_f32_32x32x16_bf16; in both products the query
-// row is the MFMA column, so lane l holds scores and outputs of row l % 32
-// only and the online-softmax state stays in the lane (lanes l and l ^ 32
-// share a row and exchange only the chunk maximum).  The fp32 operands --
-// the rotated queries, pre-scaled by log2(e) / sqrt(d), and the
-// probabilities -- are split into bf16 hi + lo parts and each product runs
-// on both, so the operands keep 16 bits beyond bf16; accumulation is fp32.
-// K rows go from the cache into MFMA registers directly (each 256-byte row
-// by two lanes, 16 bytes per k-step); V rows are staged in LDS, to be read
-// transposed; the next chunk's K and V are loaded while the current one is
-// computed.  Workgroups of one (layer, request, kv head) that split its
-// query rows run on the same XCD (ids congruent mod 8) one after another,
-// so all but the first read its K and V from that XCD's L2.
+// per (layer, request, kv head) and group of up to 64 query rows (a row is a
+// (query token, query head of the group) pair; two 32-row MFMA tiles, one
+// when the rows fit in 32).  The queries are rotated at their positions,
+// pre-scaled by log2(e) / sqrt(d), split into bf16 hi + lo and stored once
+// in LDS for all four waves (XOR-swizzled, conflict-free reads).  The waves
+// take the context's 32-token chunks round-robin; each keeps a ring of
+// chunks in registers (K fragments and V rows, 16-byte loads, two lanes per
+// 256-byte row) so that while one chunk is computed the next are in flight.
+// Per chunk a wave forms S^T = K Q^T and O^T += V^T P^T with
+// v_mfma_f32_32x32x16_bf16; in both products the query row is the MFMA
+// column, so lane l holds scores and outputs of row l % 32 only and the
+// online-softmax state stays in the lane (lanes l and l ^ 32 share a row and
+// exchange only the chunk maximum).  The probabilities are split into bf16
+// hi + lo like the queries, so both products keep about 16 bits beyond bf16;
+// accumulation is fp32.  V rows pass through LDS to be read transposed.  The
+// four waves merge their softmax states through LDS at the end.  Workgroups
+// of one (layer, request, kv head) that split its query rows run on the same
+// XCD (ids congruent mod 8).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 #include "rope_math.h"
@@ -74,12 +77,21 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
 template <int QT>
 struct AttendSmem {
   union {
-    unsigned short v[kWaves][kChunk * kVPitch];     // staged V rows, per wave
+    struct {
+      // rotated, pre-scaled queries split in bf16 hi and lo: row r's 16-byte
+      // slice j (dims [8 j, +8)) at r * 16 + (j ^ (r & 15)), so the 16 rows
+      // one 16-lane group reads land in 16 different bank groups
+      u32x4 qhi[QT * 32 * 16];
+      u32x4 qlo[QT * 32 * 16];
+      unsigned short v[kWaves][kChunk * kVPitch];   // staged V rows, per wave
+    } run;
     float o[kWaves][QT * 32 * kOPitch];             // partial outputs, for the merge
   };
   float m[kWaves][QT * 32];
   float l[kWaves][QT * 32];
 };
+
+__device__ __forceinline__ int q_slot(int r, int j) { return r * 16 + (j ^ (r & 15)); }
 
 template <int QT>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
@@ -102,52 +114,49 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
   const int row0 = grp * QT * 32;
   const float kScale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
 
-  // Queries: rotate at their positions, pre-scale, split into hi + lo.
-  // k-step s covers dims [16 s + 8 h, +8) of the lane's row.
-  bf16x8 qhi[QT][8], qlo[QT][8];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int R = row0 + qt * 32 + col;
-    float x[8][8];
+  // Queries: rotated at their positions, pre-scaled, split into hi + lo,
+  // written to LDS once for all four waves.  A task is a row and a pair of
+  // slices (j, j + 8): dims d and d + 64 rotate together.
+  for (int task = tid; task < QT * 32 * 8; task += kThreads) {
+    const int rr = task >> 3, j = task & 7;
+    const int R = row0 + rr;
+    float x[2][8];
     if (R < a.rows) {
       const int t = R / G, hq = kvh * G + R % G;
       const uint16_t* qp = a.q + ((((int64_t)layer * a.n_req + r) * a.n_qtok + t) *
                                   a.n_q_heads + hq) * kD;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * h);
+      for (int half = 0; half < 2; ++half) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 8 * j + 64 * half);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const unsigned u = v[w];
-          x[s][2 * w] = __uint_as_float(u << 16);
-          x[s][2 * w + 1] = __uint_as_float(u & 0xFFFF0000u);
+          x[half][2 * w] = __uint_as_float(u << 16);
+          x[half][2 * w + 1] = __uint_as_float(u & 0xFFFF0000u);
         }
       }
       const int pos = qpos + t;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float2 g = a.g[16 * s + 8 * h + e];       // dims d and d + 64 pair up
-          const float2 cs = sincos_of_turns(pos, g.x, g.y);
-          const float u = x[s][e], w = x[s + 4][e];
-          x[s][e] = __builtin_fmaf(u, cs.x, -(w * cs.y)) * kScale;
-          x[s + 4][e] = __builtin_fmaf(w, cs.x, u * cs.y) * kScale;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float2 g = a.g[8 * j + e];
+        const float2 cs = sincos_of_turns(pos, g.x, g.y);
+        const float u = x[0][e], w = x[1][e];
+        x[0][e] = __builtin_fmaf(u, cs.x, -(w * cs.y)) * kScale;
+        x[1][e] = __builtin_fmaf(w, cs.x, u * cs.y) * kScale;
+      }
     } else {
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[s][e] = 0.f;
+      for (int e = 0; e < 8; ++e) x[0][e] = x[1][e] = 0.f;
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      split8(x[s], qhi[qt][s], qlo[qt][s]);
-      // keep the split in registers: left to itself the compiler recomputes
-      // it from x inside the chunk loop
-      asm volatile("" : "+v"(qhi[qt][s]), "+v"(qlo[qt][s]));
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 hi, lo;
+      split8(x[half], hi, lo);
+      sm.run.qhi[q_slot(rr, j + 8 * half)] = __builtin_bit_cast(u32x4, hi);
+      sm.run.qlo[q_slot(rr, j + 8 * half)] = __builtin_bit_cast(u32x4, lo);
     }
   }
+  __syncthreads();
 
   float m[QT], lsum[QT];
   float16v o[QT][4];
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
   const char* kc = static_cast<const char*>(a.kc);
   const char* vc = static_cast<const char*>(a.vc);
   const int32_t* bt = a.bt + (int64_t)r * a.max_blocks;
-  unsigned short* vs = sm.v[wave];
+  unsigned short* vs = sm.run.v[wave];
   const int n_ctx = ce - cb;
   // Element offset of this lane's K/V row in the chunk starting at c0
   // (positions past the context re-read the first one; their scores are
@@ -173,31 +182,24 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
     return (int64_t)layer * a.s_layer + (int64_t)bt[p / a.block_size] * a.s_block +
            (int64_t)(p % a.block_size) * a.s_slot + (int64_t)kvh * a.s_head;
   };
-  // The next chunk's K fragments and V rows are loaded into registers while
-  // the current one is computed.
-  bf16x8 kf[8];
-  u32x4 vr[8];
-  auto load_chunk = [&](int64_t rowe) {
+  // A ring of chunks in registers: while one is computed, the others are in
+  // flight (three for one row tile; two rows tiles leave room for two).
+  constexpr int kDepth = QT == 1 ? 3 : 2;
+  bf16x8 kf[kDepth][8];
+  u32x4 vr[kDepth][8];
+  auto issue = [&](auto B, int c0) {
+    if (c0 >= n_ctx) return;
+    const int64_t rowe = row_of(c0);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kc + (rowe + 16 * s + 8 * h) * 2));
-      vr[s] = *reinterpret_cast<const u32x4*>(vc + (rowe + 16 * s + 8 * h) * 2);
+      kf[B][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kc + (rowe + 16 * s + 8 * h) * 2));
+      vr[B][s] = *reinterpret_cast<const u32x4*>(vc + (rowe + 16 * s + 8 * h) * 2);
     }
   };
-  // With two row tiles the registers hold no second chunk: each chunk is
-  // loaded at the top of its own step.
-  constexpr bool kPrefetch = QT == 1;
-  if (kPrefetch && wave * kChunk < n_ctx) load_chunk(row_of(wave * kChunk));
-  for (int c0 = wave * kChunk; c0 < n_ctx; c0 += kWaves * kChunk) {
-    if (!kPrefetch) load_chunk(row_of(c0));
+  auto process = [&](auto B, int c0) {
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      *reinterpret_cast<u32x4*>(vs + col * kVPitch + 16 * s + 8 * h) = vr[s];
-    bf16x8 kuse[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) kuse[s] = kf[s];
-    const int c1 = c0 + kWaves * kChunk;
-    if (kPrefetch && c1 < n_ctx) load_chunk(row_of(c1));
+      *reinterpret_cast<u32x4*>(vs + col * kVPitch + 16 * s + 8 * h) = vr[B][s];
     // S^T for each row tile: element (token, row) at lane col = row,
     // reg i -> token 8 (i / 4) + 4 h + i % 4
     float16v st[QT];
@@ -206,8 +208,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
       st[qt] = float16v{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        st[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kuse[s], qhi[qt][s], st[qt], 0, 0, 0);
-        st[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kuse[s], qlo[qt][s], st[qt], 0, 0, 0);
+        const int slot = q_slot(qt * 32 + col, 2 * s + h);
+        const bf16x8 qh = __builtin_bit_cast(bf16x8, sm.run.qhi[slot]);
+        const bf16x8 ql = __builtin_bit_cast(bf16x8, sm.run.qlo[slot]);
+        st[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B][s], qh, st[qt], 0, 0, 0);
+        st[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B][s], ql, st[qt], 0, 0, 0);
       }
     }
     // online softmax (base 2); P split for the second product
@@ -272,6 +277,26 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
         }
       }
     }
+  };
+  const int step = kWaves * kChunk;
+  const std::integral_constant<int, 0> b0;
+  const std::integral_constant<int, 1> b1;
+  const std::integral_constant<int, kDepth - 1> b2;   // the third buffer when kDepth == 3
+  int c = wave * kChunk;
+  issue(b0, c);
+  issue(b1, c + step);
+  if constexpr (kDepth == 3) issue(b2, c + 2 * step);
+  for (; c < n_ctx; c += kDepth * step) {
+    process(b0, c);
+    issue(b0, c + kDepth * step);
+    if (c + step >= n_ctx) break;
+    process(b1, c + step);
+    issue(b1, c + (kDepth + 1) * step);
+    if constexpr (kDepth == 3) {
+      if (c + 2 * step >= n_ctx) break;
+      process(b2, c + 2 * step);
+      issue(b2, c + 5 * step);
+    }
   }
 
   // merge the four waves' states
@@ -316,12 +341,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendLaunch a) {
 hipError_t launch_attend(const AttendLaunch& in, hipStream_t stream) {
   if (in.n_units == 0 || in.rows == 0) return hipSuccess;
   AttendLaunch a = in;
-  // one 32-row tile per workgroup: with the next chunk double-buffered in
-  // registers, two tiles would not fit the register file
-#ifndef IS_ATTEND_QT
-#define IS_ATTEND_QT 2
-#endif
-  const int qt = a.rows <= 32 ? 1 : IS_ATTEND_QT;
+  const int qt = a.rows <= 32 ? 1 : 2;
   a.groups = (a.rows + qt * 32 - 1) / (qt * 32);
   const int64_t wgs = (a.n_units + 7) / 8 * 8 * a.groups;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
