@@ -210,6 +210,90 @@ def attend_rate(torch, K, synth, st, w, cdesc, rope, prefix, seg_tokens, bt, str
             "TFLOPs": round(flops / (ms / 1e3) / 1e12, 2)}
 
 
+def host_tier_latency(torch, K, W, Hn, reps: int) -> dict:
+    """One request, top-50, on the Qwen3-14B-shaped store with half of the
+    facts in pinned host memory: latency of the host path, of the device
+    path and of the inject alone; the same inject with every host-tier fact
+    swapped for an HBM fact of the same length (the cost of the offload);
+    and the pinned host-to-device copy rate of the same box."""
+    w = W.WORKLOADS["qwen3_14b_offload"]
+    lens = W.fact_lengths(w)
+    n_hbm = int(len(lens) * (1 - w.host_fraction))
+    budget = int(lens[:n_hbm].sum()) * w.token_bytes * 2
+    stream = torch.cuda.current_stream()
+    st = Hn.make_store(w, lens, hbm_budget=budget)
+    try:
+        q = torch.from_numpy(W.query_embeddings(w).view(np.int16)).cuda()
+        k = w.k
+        ids_d = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        sc_d = torch.empty((1, k), dtype=torch.float32, device="cuda")
+        K.is_topk(st.handle, q, 1, k, ids_d, sc_d, stream)
+        req_off, flat = Hn.requests_from_ids(ids_d.cpu().numpy())
+        prefix = W.request_prefixes(w)
+        bt = Hn.block_tables_for(w, st.lens, req_off, flat, prefix)
+        cache = Hn.make_cache(w)
+        cdesc, rope = cache.desc, Hn.rope_of(w)
+        ids_h = torch.empty((1, k), dtype=torch.int32, pin_memory=True)
+        status = torch.full((1,), 1, dtype=torch.int32, device="cuda")
+        d_prefix = torch.from_numpy(prefix.astype(np.int32)).cuda()
+        d_bt = torch.from_numpy(bt).cuda()
+        # every host-tier fact swapped for an unused HBM fact of the same length
+        hbm_flat = flat.copy()
+        used = set(flat.tolist())
+        for j, f in enumerate(flat):
+            if f >= n_hbm:
+                g = next(int(x) for x in np.flatnonzero(lens[:n_hbm] == lens[f]) if int(x) not in used)
+                used.add(g)
+                hbm_flat[j] = g
+
+        def host():
+            K.is_topk(st.handle, q, 1, k, ids_d, sc_d, stream)
+            ids_h.copy_(ids_d, non_blocking=True)
+            stream.synchronize()
+            K.is_inject(st.handle, req_off, ids_h.numpy().reshape(-1), prefix, bt, cdesc, rope,
+                        stream)
+            stream.synchronize()
+
+        def dev():
+            K.is_retrieve_inject(st.handle, q, 1, k, d_prefix, d_bt, cdesc, rope, status, None,
+                                 stream)
+            stream.synchronize()
+
+        def inject(ids):
+            def run():
+                K.is_inject(st.handle, req_off, ids, prefix, bt, cdesc, rope, stream)
+                stream.synchronize()
+            return run
+
+        t_host = median_ms(torch, host, reps)
+        t_dev = median_ms(torch, dev, reps)
+        assert int(status.item()) == 0, "device-side validation failed"
+        t_mixed = median_ms(torch, inject(flat), reps)
+        t_hbm = median_ms(torch, inject(hbm_flat), reps)
+        tokens = int(lens[flat].sum())
+        host_tokens = int(lens[flat[flat >= n_hbm]].sum())
+        host_bytes = host_tokens * w.token_bytes * 2
+        # pinned host -> device copy rate
+        src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        t_copy = median_ms(torch, lambda: (dst.copy_(src, non_blocking=True),
+                                           stream.synchronize()), 3)
+        h2d = (1 << 30) / (t_copy / 1e3) / 1e9
+        del cache
+    finally:
+        st.destroy()
+    return {"workload": f"qwen3_14b_offload: 40 layers x 8 kv_heads x 128 bf16, 16000 facts "
+                        f"(lengths 12-64), half pinned on the host; 1 request, top-{k}",
+            "tokens": tokens, "host_tier_facts": int((flat >= n_hbm).sum()),
+            "host_tier_bytes": host_bytes,
+            "host_path_ms": round(t_host, 4), "device_path_ms": round(t_dev, 4),
+            "inject_ms": round(t_mixed, 4), "inject_all_hbm_ms": round(t_hbm, 4),
+            "offload_cost_ms": round(t_mixed - t_hbm, 4),
+            "pinned_h2d_GBps": round(h2d, 1),
+            "host_tier_GBps": round(host_bytes / ((t_mixed - t_hbm) / 1e3) / 1e9, 1)
+            if t_mixed > t_hbm else None}
+
+
 def copy_bandwidth(torch, gib: float = 4.0, reps: int = 5) -> float:
     """Plain device copy (read + write) in GB/s."""
     n = int(gib * (1 << 30))
@@ -291,6 +375,8 @@ def main() -> int:
                     help="only run the top-k over 1M x 1024 embeddings (for profiling)")
     ap.add_argument("--skip-topk-1m", action="store_true",
                     help="leave out the top-k over 1M x 1024 embeddings")
+    ap.add_argument("--skip-host-tier", action="store_true",
+                    help="leave out the single-request host-tier latency")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the path on a single MI355X; "
@@ -428,6 +514,18 @@ def main() -> int:
                "sample": desc}
     st.destroy()
     del cache
+    torch.cuda.empty_cache()
+    host_tier = None
+    if not args.skip_host_tier:
+        log("host tier: one request on the Qwen3-14B-shaped store, half pinned on the host")
+        try:
+            host_tier = host_tier_latency(torch, K, W, Hn, max(args.steps, 5))
+            log(f"host tier: inject {host_tier['inject_ms']:.3f} ms "
+                f"(all-HBM {host_tier['inject_all_hbm_ms']:.3f} ms), host path "
+                f"{host_tier['host_path_ms']:.3f} ms, device path {host_tier['device_path_ms']:.3f} ms")
+        except Exception as e:     # a box that cannot pin the tier
+            host_tier = {"error": f"{type(e).__name__}: {e}"}
+            log(f"host tier skipped: {host_tier['error']}")
     topk_1m = None
     if not args.skip_topk_1m:
         log("top-k over 1M x 1024 embeddings")
@@ -480,6 +578,7 @@ def main() -> int:
         "topk_1m": topk_1m,
         "device_path": dev,
         "attend": attend,
+        "host_tier": host_tier,
         "copy_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
     }

@@ -91,6 +91,14 @@ WORKLOADS = {
     "qwen7b_offload": Workload("qwen7b_offload", 28, 4, 128, BF16, 1_000_000,
                                ("uniform", 1, 3), 1024, 100, 50, "topk",
                                (16, 256), 16, 8_192, 1e6, host_fraction=0.5),
+    # Qwen3-14B-shaped (shape from the public model card: 40 layers, 8 kv
+    # heads, head_dim 128, RoPE theta 1e6): one request, top-50, half of the
+    # 16,000 facts (lengths 12-64) in pinned host memory -- the single-request
+    # latency of injecting from the host tier.  K+V: 163,840 B per token,
+    # about 50 GB on each tier.
+    "qwen3_14b_offload": Workload("qwen3_14b_offload", 40, 8, 128, BF16, 16_000,
+                                  ("uniform", 12, 64), 1024, 1, 50, "topk",
+                                  (32, 32), 16, 512, 1e6, host_fraction=0.5),
 }
 
 

@@ -148,3 +148,42 @@ def test_qwen7b_offload(gpu):
         Hn.check_untouched(cache, slots)
     finally:
         st.destroy()
+
+
+def test_qwen3_14b_one_request_from_both_tiers(gpu):
+    """Qwen3-14B-shaped store (half of the facts pinned on the host): one
+    request, top-50, injected by the host path and by the device path; both
+    caches equal and match the oracle on every block the request uses."""
+    import torch
+    w = W.WORKLOADS["qwen3_14b_offload"]
+    if not _host_tier_fits(w):
+        pytest.skip("host memory too small for the pinned tier")
+    lens = W.fact_lengths(w)
+    n_hbm = int(len(lens) * (1 - w.host_fraction))
+    budget = int(lens[:n_hbm].sum()) * w.token_bytes * 2
+    Hn.log(f"qwen3-14b: building the store ({budget / 1e9:.0f} GB HBM + the rest pinned)")
+    st = Hn.make_store(w, lens, hbm_budget=budget)
+    try:
+        q = W.query_embeddings(w)
+        ids, sc = Hn.gpu_topk(st, q, w.k)
+        Hn.check_topk(q, st.emb, ids, sc, w.k)
+        req_off, flat = Hn.requests_from_ids(ids)
+        Hn.log(f"  {int((flat >= n_hbm).sum())} of 50 facts on the host tier")
+        assert (flat >= n_hbm).any() and (flat < n_hbm).any()
+        prefix = W.request_prefixes(w)
+        bt = Hn.block_tables_for(w, st.lens, req_off, flat, prefix)
+        c_host = Hn.make_cache(w)
+        c_dev = Hn.make_cache(w)
+        Hn.gpu_inject(st, c_host, req_off, flat, prefix, bt)
+        status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+        Hn.K.is_retrieve_inject(st.handle, torch.from_numpy(q.view(np.int16)).cuda(), 1, w.k,
+                                torch.from_numpy(prefix.astype(np.int32)).cuda(),
+                                torch.from_numpy(bt).cuda(), c_dev.desc, Hn.rope_of(w), status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert torch.equal(c_host.k, c_dev.k) and torch.equal(c_host.v, c_dev.v)
+        n, err = Hn.check_inject_blocks(c_dev, st.lens, req_off, flat, prefix, bt,
+                                        Hn.blocks_of(bt, [0]))
+        Hn.log(f"  {n} K elements vs oracle, max err {err:.3g}")
+    finally:
+        st.destroy()
