@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
                                 + [c.c_void_p] * 4 + [c.c_int, c.c_int, c.c_int64]
                                 + [c.c_void_p] * 2 + [c.c_int64] * 4 + [c.c_void_p] * 2)
         L.or_attend.restype = c.c_int
+        L.or_ingest.argtypes = [c.c_int] * 5 + [c.c_void_p, c.c_int, c.c_void_p, c.c_void_p]
         _lib = L
     return _lib
 
@@ -197,4 +198,16 @@ def attend(n_layers, n_kv_heads, n_q_heads, d, dtype, q, qpos, ctx_begin, ctx_en
                          *strides, _p(f), _p(out))
     if rc != 0:
         raise ValueError("oracle attend: position outside the block table or cache")
+    return out
+
+
+def ingest(n_layers, n_heads, d, lens, window, enc) -> np.ndarray:
+    """Store blocks of n facts from their window encodings (see or_ingest);
+    enc: 1-D array of the encodings back to back (uint16 bf16 bits or
+    float32); returns the same dtype."""
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    enc = np.ascontiguousarray(enc)
+    out = np.empty(int(lens.sum()) * n_layers * n_heads * d, dtype=enc.dtype)
+    lib().or_ingest(n_layers, n_heads, d, enc.itemsize, len(lens), _p(lens), window, _p(enc),
+                    _p(out))
     return out

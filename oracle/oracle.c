@@ -15,6 +15,9 @@
  *     paged KV cache;
  *   - Contributions, "GPU-native system design": retrieval over a
  *     GPU-resident index picks the facts (here: exact inner-product top-k);
+ *   - Offline phase, context-window encoding: a fact is encoded behind a
+ *     window of preceding tokens and only its own tokens are stored
+ *     (or_ingest);
  *   - Online phase, query-only prefill: the engine then runs attention of
  *     the query over the cache holding the injected facts (here: synthetic
  *     queries, softmax attention with grouped kv heads, or_attend).
@@ -397,4 +400,32 @@ EXPORT int or_attend(int n_layers, int n_kv_heads, int n_q_heads, int d, int dty
       free(row);
     }
   return bad ? -1 : 0;
+}
+
+/* ----------------------------------------------------------------- ingest */
+
+/*
+ * Packing of context-window-encoded facts into the store layout (Offline
+ * phase: each fact is encoded behind a window of w preceding tokens, and
+ * only the fact's own tokens' pre-RoPE keys and values are kept).  Input:
+ * the n facts' encodings back to back, fact i as [layer][kv_head][w +
+ * len[i]][d]; output: the facts' store blocks back to back, fact i as
+ * [layer][kv_head][len[i]][d] -- the token rows w .. w + len[i] - 1 of each
+ * (layer, kv_head), bit for bit.  Elements of `es` bytes.
+ */
+EXPORT void or_ingest(int n_layers, int n_heads, int d, int es, int n, const int32_t* len,
+                      int w, const void* enc, void* out) {
+  const char* src = (const char*)enc;
+  char* dst = (char*)out;
+  for (int i = 0; i < n; ++i) {
+    for (int l = 0; l < n_layers; ++l)
+      for (int h = 0; h < n_heads; ++h)
+        for (int t = 0; t < len[i]; ++t) {
+          const int64_t s_row = ((int64_t)(l * n_heads + h) * (w + len[i]) + w + t) * d;
+          const int64_t d_row = ((int64_t)(l * n_heads + h) * len[i] + t) * d;
+          memcpy(dst + d_row * es, src + s_row * es, (size_t)d * es);
+        }
+    src += (int64_t)n_layers * n_heads * (w + len[i]) * d * es;
+    dst += (int64_t)n_layers * n_heads * len[i] * d * es;
+  }
 }

@@ -35,6 +35,9 @@ MUTANTS = {
                               "or_rotate(x, d, (double)qpos[r], f, qr);"),
     "attend_value_source": ("* load_elem(v_cache, vb + i, dtype);",
                             "* load_elem(k_cache, vb + i, dtype);"),
+    "ingest_window": ("(w + len[i]) + w + t) * d;", "(w + len[i]) + t) * d;"),
+    "ingest_row_stride": ("const int64_t s_row = ((int64_t)(l * n_heads + h) * (w + len[i])",
+                          "const int64_t s_row = ((int64_t)(l * n_heads + h) * (len[i])"),
 }
 
 

@@ -586,3 +586,30 @@ def test_attention_rejects_positions_outside_the_table():
     with pytest.raises(ValueError):
         oracle.attend(L, H, H, d, synth.F32, q, [9], [0], [9], np.array([[0, 1]], np.int32), B,
                       nb, kc, kc, _nhd(L, nb, B, H, d), oracle.rope_freqs(d, 1e4))
+
+
+# ----------------------------------------------------------------- ingest
+# Context-window-encoded facts packed into the store layout.
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_ingest_round_trip_drops_exactly_the_window(dtype):
+    """Encodings built by placing each fact's stored rows behind w rows of
+    another sequence, per (layer, kv head): packing returns the facts' rows
+    and nothing else."""
+    L, H, d, w = 3, 2, 16, 5
+    lens = np.array([4, 1, 9], np.int32)
+    encs, facts = [], []
+    for i, n in enumerate(lens):
+        fact = synth.fact_kv(21, synth.TAG_K, i, L * H * int(n) * d, dtype).reshape(L, H, n, d)
+        window = synth.fact_kv(21, synth.TAG_V, 100 + i, L * H * w * d, dtype).reshape(L, H, w, d)
+        encs.append(np.concatenate([window, fact], axis=2).reshape(-1))
+        facts.append(fact.reshape(-1))
+    got = oracle.ingest(L, H, d, lens, w, np.concatenate(encs))
+    assert np.array_equal(got.view(np.uint8), np.concatenate(facts).view(np.uint8))
+
+
+def test_ingest_without_window_is_the_identity():
+    L, H, d = 2, 4, 8
+    lens = np.array([3, 7], np.int32)
+    enc = synth.fact_kv(22, synth.TAG_K, 0, int(lens.sum()) * L * H * d, synth.BF16)
+    assert np.array_equal(oracle.ingest(L, H, d, lens, 0, enc), enc)
