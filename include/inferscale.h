@@ -80,6 +80,9 @@ typedef struct is_store is_store;
  *                                    back to back in id order (NULL: leave
  *                                    uninitialised, fill with is_store_load)
  *   emb_src                          optional host [n_facts][emb_dim] fp16
+ *   spare_facts, spare_tokens        room kept in HBM for facts added later
+ *                                    by is_store_append (0: none); a store
+ *                                    with a host tier takes no spare room
  */
 typedef struct {
   int32_t n_layers;
@@ -94,6 +97,8 @@ typedef struct {
   const void* k_src;
   const void* v_src;
   const uint16_t* emb_src;
+  int64_t spare_facts;
+  int64_t spare_tokens;
 } is_store_desc;
 
 /*
@@ -243,6 +248,44 @@ int is_retrieve_inject(const is_store* s, const uint16_t* q_f16, int32_t n_req, 
                        const int32_t* prefix_len, const int32_t* block_tables,
                        int32_t max_blocks, const is_cache* cache, const is_rope* rope,
                        int32_t* ids_out, int32_t* status, void* stream);
+
+/*
+ * Adds n facts from their context-window encodings (Offline phase: a fact
+ * is encoded behind a window of preceding tokens, and only the fact's own
+ * tokens' pre-RoPE keys and raw values are stored).
+ *   fact_len[n]        host, each >= 1
+ *   window             tokens encoded before each fact (>= 0)
+ *   k_enc, v_enc       device, the n encodings back to back, fact i as
+ *                      [layer][kv_head][window + fact_len[i]][head_dim]
+ *                      (16-byte aligned); only rows window .. window +
+ *                      fact_len[i] - 1 of each (layer, kv_head) are stored,
+ *                      bit for bit
+ *   emb                device [n][emb_dim] fp16 (required when the store
+ *                      has an index, else NULL)
+ *   first_id           host out: the id of the first new fact (ids are
+ *                      consecutive)
+ * The new facts go to HBM, into the spare room reserved at creation.
+ * Asynchronous on `stream`: calls that use the new facts must be ordered
+ * after it on the device (same stream, or synchronized).  The sources must
+ * stay valid until the stream has completed.
+ * Errors: IS_ERR_INVALID_ARG, IS_ERR_ALIGN, IS_ERR_OOM (no spare room),
+ * IS_ERR_UNSUPPORTED (the store has a host tier), IS_ERR_HIP.
+ */
+int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, int32_t window,
+                    const void* k_enc, const void* v_enc, const uint16_t* emb,
+                    int64_t* first_id, void* stream);
+
+/*
+ * Replaces the stored K/V (and, when emb is not NULL, the embedding row) of
+ * fact `fact_id` from a new window encoding of the same length
+ * ([layer][kv_head][window + len][head_dim], device, 16-byte aligned) --
+ * a fact update; host-tier facts are rewritten in place over PCIe.
+ * Asynchronous on `stream`; the caller orders it against calls that read
+ * the fact.  Errors: IS_ERR_INVALID_ARG, IS_ERR_FACT_ID, IS_ERR_ALIGN,
+ * IS_ERR_HIP.
+ */
+int is_store_update(is_store* s, int64_t fact_id, int32_t window, const void* k_enc,
+                    const void* v_enc, const uint16_t* emb, void* stream);
 
 /*
  * Query-only attention over the paged cache, the step that follows the

@@ -25,8 +25,8 @@ IS_DTYPE_F32, IS_DTYPE_BF16 = 0, 1
 IS_ROPE_NONE, IS_ROPE_LLAMA3 = 0, 1
 
 EXPORTS = ("is_store_create", "is_store_load", "is_store_get_info", "is_topk", "is_inject",
-           "is_retrieve_inject", "is_attend", "is_inject_check", "is_store_destroy",
-           "is_last_error")
+           "is_retrieve_inject", "is_attend", "is_store_append", "is_store_update",
+           "is_inject_check", "is_store_destroy", "is_last_error")
 
 
 class ISError(RuntimeError):
@@ -41,7 +41,8 @@ class is_store_desc(ctypes.Structure):
                 ("n_facts", ctypes.c_int64), ("fact_len", ctypes.c_void_p),
                 ("emb_dim", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("hbm_budget_bytes", ctypes.c_int64), ("k_src", ctypes.c_void_p),
-                ("v_src", ctypes.c_void_p), ("emb_src", ctypes.c_void_p)]
+                ("v_src", ctypes.c_void_p), ("emb_src", ctypes.c_void_p),
+                ("spare_facts", ctypes.c_int64), ("spare_tokens", ctypes.c_int64)]
 
 
 class is_cache(ctypes.Structure):
@@ -85,6 +86,9 @@ def lib() -> ctypes.CDLL:
                                          c.POINTER(is_cache), c.POINTER(is_rope), P, P, P]
         L.is_attend.argtypes = [P, c.POINTER(is_cache), c.POINTER(is_rope), c.c_int32,
                                 c.c_int32, c.c_int32, P, P, P, P, P, c.c_int32, P, P]
+        L.is_store_append.argtypes = [P, c.c_int32, P, c.c_int32, P, P, P,
+                                      c.POINTER(c.c_int64), P]
+        L.is_store_update.argtypes = [P, c.c_int64, c.c_int32, P, P, P, P]
         L.is_inject_check.argtypes = [c.POINTER(is_store_desc), c.c_int32, P, P, P, P,
                                       c.c_int32, c.POINTER(is_cache), c.POINTER(is_rope),
                                       c.POINTER(c.c_int64)]
@@ -131,7 +135,8 @@ def _stream(s) -> int | None:
 
 
 def make_desc(n_layers, n_kv_heads, head_dim, kv_dtype, fact_len, emb_dim=0,
-              hbm_budget_bytes=-1, k_src=None, v_src=None, emb_src=None):
+              hbm_budget_bytes=-1, k_src=None, v_src=None, emb_src=None, spare_facts=0,
+              spare_tokens=0):
     """Builds an is_store_desc; returns (desc, keepalive)."""
     lens, lens_p = _host(fact_len, np.int32)
     keep = [lens]
@@ -144,7 +149,7 @@ def make_desc(n_layers, n_kv_heads, head_dim, kv_dtype, fact_len, emb_dim=0,
             keep.append(arr)
             srcs.append(arr.ctypes.data)
     d = is_store_desc(n_layers, n_kv_heads, head_dim, kv_dtype, len(lens), lens_p, emb_dim, 0,
-                      hbm_budget_bytes, *srcs)
+                      hbm_budget_bytes, *srcs, spare_facts, spare_tokens)
     return d, keep
 
 
@@ -202,6 +207,24 @@ def is_attend(store: int, cache: is_cache, rope: is_rope, q, n_qtok: int, n_q_he
     _check(lib().is_attend(store, ctypes.byref(cache), ctypes.byref(rope), len(qp), n_qtok,
                            n_q_heads, _dev(q), qp_p, cb_p, ce_p, bt.ctypes.data, bt.shape[1],
                            _dev(out), _stream(stream)))
+
+
+def is_store_append(store: int, fact_len, window: int, k_enc, v_enc, emb=None,
+                    stream=None) -> int:
+    """fact_len: host array; k_enc, v_enc (the window encodings back to back)
+    and emb ([n][emb_dim] fp16 bits) device tensors.  Returns the first new
+    fact id."""
+    fl, fl_p = _host(fact_len, np.int32)
+    first = ctypes.c_int64(-1)
+    _check(lib().is_store_append(store, len(fl), fl_p, window, _dev(k_enc), _dev(v_enc),
+                                 _dev(emb), ctypes.byref(first), _stream(stream)))
+    return first.value
+
+
+def is_store_update(store: int, fact_id: int, window: int, k_enc, v_enc, emb=None,
+                    stream=None) -> None:
+    _check(lib().is_store_update(store, fact_id, window, _dev(k_enc), _dev(v_enc), _dev(emb),
+                                 _stream(stream)))
 
 
 def make_cache(k_base, v_base, strides, block_size, n_blocks, dtype) -> is_cache:

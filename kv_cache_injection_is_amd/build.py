@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 SO = os.path.join(PKG, "libinferscale.so")
 HIPCC = "/opt/rocm/bin/hipcc"
 
-SOURCES = ["abi.hip", "inject.hip", "topk.hip", "compose.hip", "attend.hip", "plan.cpp"]
+SOURCES = ["abi.hip", "inject.hip", "topk.hip", "compose.hip", "attend.hip", "ingest.hip", "plan.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", f"-I{INCLUDE}"]
 

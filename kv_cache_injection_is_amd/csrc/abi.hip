@@ -68,6 +68,8 @@ struct is_store {
   int device = 0;
   int32_t L = 0, H = 0, d = 0, dtype = 0, emb_dim = 0;
   int64_t n_facts = 0, n_hbm = 0;
+  int64_t max_facts = 0;          // facts the tables and the embedding arena hold
+  int64_t hbm_tokens = 0;         // tokens the HBM arenas hold
   std::vector<int32_t> len;
   std::vector<int64_t> tok_off;   // [n_facts + 1]
   size_t es = 0;
@@ -91,6 +93,9 @@ struct is_store {
   // Bytes of the blocked embeddings (whole tiles, padded width).
   size_t emb_bytes() const {
     return (size_t)is::topk_padded_facts(n_facts) * is::topk_padded_dim(emb_dim) * 2;
+  }
+  size_t emb_alloc_bytes() const {
+    return (size_t)is::topk_padded_facts(max_facts) * is::topk_padded_dim(emb_dim) * 2;
   }
   size_t fact_bytes(int64_t f0, int64_t f1) const {
     return (size_t)(tok_off[f1] - tok_off[f0]) * row_elems() * es;
@@ -234,7 +239,14 @@ IS_EXPORT int is_store_create(const is_store_desc* d, is_store** out) {
     s->n_hbm = std::upper_bound(s->tok_off.begin(), s->tok_off.end(), max_tok) -
                s->tok_off.begin() - 1;
   }
-  const size_t hbm_bytes = s->fact_bytes(0, s->n_hbm);
+  // Spare room for appended facts: HBM only, and only without a host tier.
+  if ((d->spare_facts > 0 || d->spare_tokens > 0) && s->n_hbm < s->n_facts) {
+    free_store(s);
+    return fail(IS_ERR_UNSUPPORTED, "spare room for appends needs a store without a host tier");
+  }
+  s->max_facts = s->n_facts + std::max<int64_t>(d->spare_facts, 0);
+  s->hbm_tokens = s->tok_off[s->n_hbm] + std::max<int64_t>(d->spare_tokens, 0);
+  const size_t hbm_bytes = (size_t)s->hbm_tokens * s->row_elems() * s->es;
   if (hbm_bytes > 0 && (hipMalloc(&s->k_dev, hbm_bytes) != hipSuccess ||
                         hipMalloc(&s->v_dev, hbm_bytes) != hipSuccess)) {
     free_store(s);
@@ -279,9 +291,10 @@ IS_EXPORT int is_store_create(const is_store_desc* d, is_store** out) {
   }
   {
     const size_t n = (size_t)s->n_facts;
-    if (hipMalloc((void**)&s->d_len, n * 4) != hipSuccess ||
-        hipMalloc((void**)&s->d_k_addr, n * 8) != hipSuccess ||
-        hipMalloc((void**)&s->d_v_addr, n * 8) != hipSuccess) {
+    const size_t cap = (size_t)s->max_facts;
+    if (hipMalloc((void**)&s->d_len, cap * 4) != hipSuccess ||
+        hipMalloc((void**)&s->d_k_addr, cap * 8) != hipSuccess ||
+        hipMalloc((void**)&s->d_v_addr, cap * 8) != hipSuccess) {
       free_store(s);
       return fail(IS_ERR_OOM, "device allocation of the fact tables failed");
     }
@@ -293,7 +306,7 @@ IS_EXPORT int is_store_create(const is_store_desc* d, is_store** out) {
     }
   }
   if (s->emb_dim > 0) {
-    const size_t bytes = s->emb_bytes();
+    const size_t bytes = s->emb_alloc_bytes();
     if (hipMalloc((void**)&s->emb, bytes) != hipSuccess) {
       free_store(s);
       return fail(IS_ERR_OOM, "device allocation of the embeddings failed");
@@ -737,6 +750,157 @@ IS_EXPORT int is_attend(const is_store* cs, const is_cache* cache, const is_rope
   a.rows = n_qtok * (n_q_heads / s->H);
   a.n_units = (int64_t)s->L * n_req * s->H;
   if ((e = is::launch_attend(a, st)) != hipSuccess) return hip_fail(e, "attention launch");
+  if ((e = hipEventRecord(sl->done, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return IS_OK;
+}
+
+namespace {
+
+// Stages `items` and launches the packing copy, 65535 facts per launch.
+int launch_ingest_items(is_store* s, const std::vector<is::IngestItem>& items, size_t extra_bytes,
+                        const void* extra, hipStream_t st, Slot** out_slot, char** extra_dev) {
+  const size_t items_bytes = align256(items.size() * sizeof(is::IngestItem));
+  Slot* sl = nullptr;
+  int rc = acquire_slot(s, items_bytes + extra_bytes, &sl);
+  if (rc != IS_OK) return rc;
+  std::memcpy(sl->host, items.data(), items.size() * sizeof(is::IngestItem));
+  if (extra_bytes) std::memcpy(static_cast<char*>(sl->host) + items_bytes, extra, extra_bytes);
+  hipError_t e = hipMemcpyAsync(sl->dev, sl->host, items_bytes + extra_bytes,
+                                hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "staging copy");
+  const is::IngestItem* dev_items = static_cast<const is::IngestItem*>(sl->dev);
+  for (size_t i0 = 0; i0 < items.size(); i0 += 65535) {
+    is::IngestLaunch a{};
+    a.items = dev_items + i0;
+    a.n_items = (int32_t)std::min<size_t>(65535, items.size() - i0);
+    a.n_layers = s->L;
+    a.n_heads = s->H;
+    a.row_bytes = (int32_t)(s->d * s->es);
+    if ((e = is::launch_ingest(a, st)) != hipSuccess) return hip_fail(e, "ingest launch");
+  }
+  *out_slot = sl;
+  *extra_dev = static_cast<char*>(sl->dev) + items_bytes;
+  return IS_OK;
+}
+
+}  // namespace
+
+IS_EXPORT int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, int32_t window,
+                              const void* k_enc, const void* v_enc, const uint16_t* emb,
+                              int64_t* first_id, void* stream) {
+  is::clear_error();
+  if (s == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  if (first_id == nullptr) return fail(IS_ERR_INVALID_ARG, "null first_id");
+  if (n < 0 || window < 0) return fail(IS_ERR_INVALID_ARG, "n and window must be >= 0");
+  if (s->n_hbm < s->n_facts)
+    return fail(IS_ERR_UNSUPPORTED, "appends need a store without a host tier");
+  *first_id = s->n_facts;
+  if (n == 0) return IS_OK;
+  if (fact_len == nullptr || k_enc == nullptr || v_enc == nullptr)
+    return fail(IS_ERR_INVALID_ARG, "null fact_len or encoding");
+  if (s->emb_dim > 0 && emb == nullptr)
+    return fail(IS_ERR_INVALID_ARG, "the store has an index: the new facts need embeddings");
+  if (((uintptr_t)k_enc & 15u) || ((uintptr_t)v_enc & 15u) || ((uintptr_t)emb & 15u))
+    return fail(IS_ERR_ALIGN, "encodings and embeddings must be 16-byte aligned");
+  int64_t tokens = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (fact_len[i] < 1) return fail(IS_ERR_INVALID_ARG, "fact lengths must be >= 1");
+    if ((int64_t)window + fact_len[i] > ((int64_t)1 << 24))
+      return fail(IS_ERR_INVALID_ARG, "window + fact length must stay below 2^24");
+    tokens += fact_len[i];
+  }
+  DeviceGuard guard(s->device);
+  std::lock_guard<std::mutex> lock(s->mu);
+  const int64_t f0 = s->n_facts;
+  if (f0 + n > s->max_facts || s->tok_off[f0] + tokens > s->hbm_tokens)
+    return fail(IS_ERR_OOM, "no spare room left in the store for these facts");
+  // new facts' blocks follow the last fact in the HBM arenas
+  std::vector<is::IngestItem> items((size_t)n);
+  std::vector<int32_t> new_len(fact_len, fact_len + n);
+  std::vector<uint64_t> new_k((size_t)n), new_v((size_t)n);
+  int64_t tok = s->tok_off[f0];
+  size_t src = 0;
+  const size_t row = (size_t)s->row_elems() * s->es;   // one token over all layers and heads
+  for (int32_t i = 0; i < n; ++i) {
+    is::IngestItem& it = items[(size_t)i];
+    it.src_k = static_cast<const char*>(k_enc) + src;
+    it.src_v = static_cast<const char*>(v_enc) + src;
+    it.dst_k = static_cast<char*>(s->k_dev) + (size_t)tok * row;
+    it.dst_v = static_cast<char*>(s->v_dev) + (size_t)tok * row;
+    it.len = fact_len[i];
+    it.window = window;
+    new_k[(size_t)i] = (uint64_t)(uintptr_t)it.dst_k;
+    new_v[(size_t)i] = (uint64_t)(uintptr_t)it.dst_v;
+    src += (size_t)(window + fact_len[i]) * row;
+    tok += fact_len[i];
+  }
+  // the device fact tables' new entries travel with the work list
+  const size_t tab_bytes = (size_t)n * (4 + 8 + 8);
+  std::vector<char> tables(tab_bytes);
+  std::memcpy(tables.data(), new_len.data(), (size_t)n * 4);
+  std::memcpy(tables.data() + (size_t)n * 4, new_k.data(), (size_t)n * 8);
+  std::memcpy(tables.data() + (size_t)n * 12, new_v.data(), (size_t)n * 8);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Slot* sl = nullptr;
+  char* tab_dev = nullptr;
+  int rc = launch_ingest_items(s, items, tab_bytes, tables.data(), st, &sl, &tab_dev);
+  if (rc != IS_OK) return rc;
+  hipError_t e;
+  if ((e = hipMemcpyAsync(s->d_len + f0, tab_dev, (size_t)n * 4, hipMemcpyDeviceToDevice, st)) !=
+          hipSuccess ||
+      (e = hipMemcpyAsync(s->d_k_addr + f0, tab_dev + (size_t)n * 4, (size_t)n * 8,
+                          hipMemcpyDeviceToDevice, st)) != hipSuccess ||
+      (e = hipMemcpyAsync(s->d_v_addr + f0, tab_dev + (size_t)n * 12, (size_t)n * 8,
+                          hipMemcpyDeviceToDevice, st)) != hipSuccess)
+    return hip_fail(e, "fact table update");
+  if (s->emb_dim > 0 && (e = is::launch_emb_relayout(emb, f0, n, s->emb_dim, s->emb, st)) !=
+                            hipSuccess)
+    return hip_fail(e, "embedding relayout");
+  if ((e = hipEventRecord(sl->done, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  // host tables last: every step above has been enqueued
+  for (int32_t i = 0; i < n; ++i) {
+    s->len.push_back(fact_len[i]);
+    s->tok_off.push_back(s->tok_off.back() + fact_len[i]);
+    s->k_addr.push_back(new_k[(size_t)i]);
+    s->v_addr.push_back(new_v[(size_t)i]);
+  }
+  s->n_facts += n;
+  s->n_hbm += n;
+  return IS_OK;
+}
+
+IS_EXPORT int is_store_update(is_store* s, int64_t fact_id, int32_t window, const void* k_enc,
+                              const void* v_enc, const uint16_t* emb, void* stream) {
+  is::clear_error();
+  if (s == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  if (fact_id < 0 || fact_id >= s->n_facts) return fail(IS_ERR_FACT_ID, "fact id out of range");
+  if (window < 0) return fail(IS_ERR_INVALID_ARG, "window must be >= 0");
+  if (k_enc == nullptr || v_enc == nullptr) return fail(IS_ERR_INVALID_ARG, "null encoding");
+  if (((uintptr_t)k_enc & 15u) || ((uintptr_t)v_enc & 15u) || ((uintptr_t)emb & 15u))
+    return fail(IS_ERR_ALIGN, "encodings and embeddings must be 16-byte aligned");
+  if (emb != nullptr && s->emb_dim == 0)
+    return fail(IS_ERR_INVALID_ARG, "store has no embedding index");
+  const int32_t len = s->len[(size_t)fact_id];
+  if ((int64_t)window + len > ((int64_t)1 << 24))
+    return fail(IS_ERR_INVALID_ARG, "window + fact length must stay below 2^24");
+  DeviceGuard guard(s->device);
+  std::lock_guard<std::mutex> lock(s->mu);
+  std::vector<is::IngestItem> items(1);
+  items[0].src_k = static_cast<const char*>(k_enc);
+  items[0].src_v = static_cast<const char*>(v_enc);
+  items[0].dst_k = reinterpret_cast<char*>((uintptr_t)s->k_addr[(size_t)fact_id]);
+  items[0].dst_v = reinterpret_cast<char*>((uintptr_t)s->v_addr[(size_t)fact_id]);
+  items[0].len = len;
+  items[0].window = window;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Slot* sl = nullptr;
+  char* unused = nullptr;
+  int rc = launch_ingest_items(s, items, 0, nullptr, st, &sl, &unused);
+  if (rc != IS_OK) return rc;
+  hipError_t e;
+  if (emb != nullptr &&
+      (e = is::launch_emb_relayout(emb, fact_id, 1, s->emb_dim, s->emb, st)) != hipSuccess)
+    return hip_fail(e, "embedding relayout");
   if ((e = hipEventRecord(sl->done, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return IS_OK;
 }

@@ -76,6 +76,22 @@ struct AttendLaunch {
 
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t stream);
 
+// Packing of a window-encoded fact into its store block.
+struct IngestItem {
+  const char* src_k;        // encoding [layer][kv_head][window + len][head_dim]
+  const char* src_v;
+  char* dst_k;              // store block [layer][kv_head][len][head_dim]
+  char* dst_v;
+  int32_t len, window;
+  int32_t reserved[2];
+};
+static_assert(sizeof(IngestItem) == 48, "IngestItem layout");
+struct IngestLaunch {
+  const IngestItem* items;  // [n_items], at most 65535 per launch
+  int32_t n_items, n_layers, n_heads, row_bytes;
+};
+hipError_t launch_ingest(const IngestLaunch& a, hipStream_t stream);
+
 // Top-k geometry.  The store keeps the embeddings tile-blocked,
 // [tile of 256 facts][64-dim chunk][256 rows][64] fp16, with the width
 // padded to a multiple of 64 and rows past n_facts zero, so that every

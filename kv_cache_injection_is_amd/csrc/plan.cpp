@@ -60,6 +60,11 @@ int check_store_desc(const is_store_desc* d) {
   for (int64_t f = 0; f < d->n_facts; ++f)
     if (d->fact_len[f] < 1)
       return fail(IS_ERR_INVALID_ARG, "fact " + std::to_string(f) + " has length < 1");
+  if (d->spare_facts < 0 || d->spare_tokens < 0)
+    return fail(IS_ERR_INVALID_ARG, "spare_facts and spare_tokens must be >= 0");
+  if (d->n_facts + d->spare_facts > INT32_MAX)
+    return fail(IS_ERR_INVALID_ARG, "n_facts + spare_facts must fit int32");
+  if (d->emb_dim > 16384) return fail(IS_ERR_UNSUPPORTED, "emb_dim must be <= 16384");
   if (d->emb_dim < 0 || d->emb_dim % 32 != 0)
     return fail(d->emb_dim < 0 ? IS_ERR_INVALID_ARG : IS_ERR_UNSUPPORTED,
                 "emb_dim must be 0 or a positive multiple of 32");

@@ -240,11 +240,12 @@ def k_tolerance(ref: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def oracle_blocks(w: W.Workload, lens, req_off, flat_ids, prefix, bt, blocks, layout,
-                  cache_nb):
+                  cache_nb, rows=None):
     """Runs the oracle on the given requests into a compact host cache that
     holds only `blocks` (physical ids, remapped to 0..m-1), initialised to
     the same sentinel the GPU cache was filled with.  Returns (k, v) arrays
-    [L][m][B*H*d] in the cache's layout, raw bytes."""
+    [L][m][B*H*d] in the cache's layout, raw bytes.  `rows` maps a fact id
+    to its (K, V) store blocks where they are not the generator's."""
     L, H, d, B, es = w.n_layers, w.n_kv_heads, w.head_dim, w.block_size, w.elem_size
     uniq = np.unique(flat_ids)
     remap = {int(f): i for i, f in enumerate(uniq)}
@@ -253,10 +254,14 @@ def oracle_blocks(w: W.Workload, lens, req_off, flat_ids, prefix, bt, blocks, la
     np.cumsum(sub_lens, out=sub_off[1:])
     row = w.row_elems
     empty = [np.zeros(1, dtype=synth.kv_dtype_np(w.dtype))]
-    Kh = np.concatenate([synth.fact_kv(w.seed, synth.TAG_K, int(f), int(lens[f]) * row, w.dtype)
-                         for f in uniq] or empty)
-    Vh = np.concatenate([synth.fact_kv(w.seed, synth.TAG_V, int(f), int(lens[f]) * row, w.dtype)
-                         for f in uniq] or empty)
+    rows = rows or {}
+
+    def block(f, tag, i):
+        if int(f) in rows:
+            return rows[int(f)][i]
+        return synth.fact_kv(w.seed, tag, int(f), int(lens[f]) * row, w.dtype)
+    Kh = np.concatenate([block(f, synth.TAG_K, 0) for f in uniq] or empty)
+    Vh = np.concatenate([block(f, synth.TAG_V, 1) for f in uniq] or empty)
     blocks = np.asarray(blocks, dtype=np.int64)
     bmap = {int(b): i for i, b in enumerate(blocks)}
     bt_c = np.vectorize(lambda b: bmap.get(int(b), -1))(bt).astype(np.int32)
@@ -310,13 +315,14 @@ def gpu_blocks(cache: Cache, blocks):
     return (kk.index_select(1, idx).cpu().numpy(), vv.index_select(1, idx).cpu().numpy())
 
 
-def check_inject_blocks(cache: Cache, lens, req_off, flat_ids, prefix, bt, blocks):
+def check_inject_blocks(cache: Cache, lens, req_off, flat_ids, prefix, bt, blocks, rows=None):
     """Element-by-element comparison of the GPU cache and the oracle on the
-    given physical blocks (all layers).  Returns (#elements compared, max K error)."""
+    given physical blocks (all layers).  Returns (#elements compared, max K
+    error).  `rows`: as for oracle_blocks."""
     w = cache.w
     es = w.elem_size
     kc_o, vc_o = oracle_blocks(w, lens, req_off, flat_ids, prefix, bt, blocks, cache.layout,
-                               cache.n_blocks)
+                               cache.n_blocks, rows)
     kg, vg = gpu_blocks(cache, blocks)
     mask_e, _ = touched_mask(w, lens, req_off, flat_ids, prefix, bt, blocks, cache.layout)
     L, m = w.n_layers, len(blocks)

@@ -1,0 +1,141 @@
+"""Store ingest through the C ABI: facts packed from context-window
+encodings (is_store_append, is_store_update), checked by injecting them and
+comparing with the oracle run on the facts' own rows, and by top-k finding
+the appended embeddings."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import workloads as W
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+L, H, D, B = 4, 2, 128, 16
+EMB = 64
+SEED = 31
+WINDOW = 7
+
+
+@pytest.fixture(autouse=True)
+def _gpu_cleanup(gpu):
+    yield
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _workload(n_facts):
+    return W.WORKLOADS["llama8b_batch"].scaled(name="ingest", n_layers=L, n_kv_heads=H,
+                                               head_dim=D, n_facts=n_facts, emb_dim=EMB,
+                                               block_size=B, n_blocks=64, seed=SEED)
+
+
+def _encodings(entities, lens, window, tag):
+    """Each fact's rows (from the generator, entity e) behind `window` rows
+    of another sequence, per (layer, kv head); returns (encodings back to
+    back, the facts' rows back to back)."""
+    encs, rows = [], []
+    for e, n in zip(entities, lens):
+        fact = synth.fact_kv(SEED, tag, int(e), L * H * int(n) * D, synth.BF16).reshape(L, H, n, D)
+        pre = synth.fact_kv(SEED, tag, 50_000 + int(e), L * H * window * D,
+                            synth.BF16).reshape(L, H, window, D)
+        encs.append(np.concatenate([pre, fact], axis=2).reshape(-1))
+        rows.append(fact.reshape(-1))
+    return np.concatenate(encs), np.concatenate(rows)
+
+
+def _inject_and_check(st, w, cache, lens_all, ids, rows):
+    """Injects facts `ids` (one request, prefix 5) and compares the touched
+    blocks with the oracle run on `rows` (fact -> (K, V) store blocks) for
+    the facts packed from encodings, the generator's for the rest."""
+    import torch
+    req_off = np.array([0, len(ids)], np.int32)
+    flat = np.asarray(ids, np.int32)
+    prefix = np.array([5], np.int32)
+    bt = Hn.block_tables_for(w, lens_all, req_off, flat, prefix)
+    Hn.gpu_inject(st, cache, req_off, flat, prefix, bt)
+    torch.cuda.synchronize()
+    n, err = Hn.check_inject_blocks(cache, lens_all, req_off, flat, prefix, bt,
+                                    Hn.blocks_of(bt, [0]), rows)
+    Hn.log(f"  {n} K elements compared, worst {err:.3g}")
+
+
+def test_append_update_and_retrieve(gpu):
+    import torch
+    w = _workload(20)
+    lens = W.fact_lengths(w)
+    row = L * H * D
+    desc, keep = Hn.K.make_desc(L, H, D, synth.BF16, lens, EMB, spare_facts=8, spare_tokens=400)
+    h = Hn.K.is_store_create(desc)
+    try:
+        # the first 20 facts through the plain loader
+        Hn.K.is_store_load(h, 0, 20, synth.kv_range(SEED, synth.TAG_K, 0, lens, row, synth.BF16),
+                           synth.kv_range(SEED, synth.TAG_V, 0, lens, row, synth.BF16),
+                           synth.embeddings(SEED, 0, 20, EMB))
+        # six more from window encodings, ragged (1 to 40 tokens)
+        new_lens = np.array([3, 17, 1, 40, 9, 25], np.int32)
+        ent = np.arange(100, 106)
+        k_enc, k_rows = _encodings(ent, new_lens, WINDOW, synth.TAG_K)
+        v_enc, v_rows = _encodings(ent, new_lens, WINDOW, synth.TAG_V)
+        k_ora = oracle.ingest(L, H, D, new_lens, WINDOW, k_enc)
+        v_ora = oracle.ingest(L, H, D, new_lens, WINDOW, v_enc)
+        assert np.array_equal(k_ora, k_rows) and np.array_equal(v_ora, v_rows)
+        emb_new = synth.embeddings(SEED, 100, 6, EMB)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+        Hn.log(f"ingest: append {list(new_lens)} behind a window of {WINDOW}")
+        first = Hn.K.is_store_append(h, new_lens, WINDOW, dev(k_enc), dev(v_enc), dev(emb_new))
+        torch.cuda.synchronize()
+        assert first == 20
+        assert Hn.K.is_store_get_info(h).n_facts == 26
+        lens_all = np.concatenate([lens, new_lens]).astype(np.int32)
+        st = Hn.Store(w, lens_all, None, h, None)
+        cut = np.concatenate([[0], np.cumsum(new_lens)]) * row
+        rows = {20 + i: (k_ora[cut[i]:cut[i + 1]], v_ora[cut[i]:cut[i + 1]]) for i in range(6)}
+        # appended facts injected next to loaded ones
+        ids = [22, 3, 25, 20, 23, 11]
+        _inject_and_check(st, w, Hn.make_cache(w), lens_all, ids, rows)
+        # top-k sees the appended embeddings: each ranks first for itself
+        got, _ = Hn.gpu_topk(st, emb_new, 1)
+        assert got[:, 0].tolist() == list(range(20, 26))
+        # fact 3 replaced in place from a window-free encoding of new values
+        Hn.log("ingest: update fact 3")
+        k_new, _ = _encodings([200], lens[3:4], 0, synth.TAG_K)
+        v_new, _ = _encodings([200], lens[3:4], 0, synth.TAG_V)
+        emb3 = synth.embeddings(SEED, 200, 1, EMB)
+        Hn.K.is_store_update(h, 3, 0, dev(k_new), dev(v_new), dev(emb3))
+        torch.cuda.synchronize()
+        rows[3] = (oracle.ingest(L, H, D, lens[3:4], 0, k_new),
+                   oracle.ingest(L, H, D, lens[3:4], 0, v_new))
+        _inject_and_check(st, w, Hn.make_cache(w), lens_all, ids, rows)
+        got, _ = Hn.gpu_topk(st, emb3, 1)
+        assert got[0, 0] == 3
+        # beyond the spare tokens (400, 95 used): out of memory, nothing appended
+        big = np.array([200, 200], np.int32)
+        k_big, _ = _encodings([300, 301], big, 0, synth.TAG_K)
+        with pytest.raises(Hn.K.ISError) as e:
+            Hn.K.is_store_append(h, big, 0, dev(k_big), dev(k_big),
+                                 dev(synth.embeddings(SEED, 300, 2, EMB)))
+        assert e.value.code == -7
+        assert Hn.K.is_store_get_info(h).n_facts == 26
+    finally:
+        Hn.K.is_store_destroy(h)
+
+
+def test_append_rejected_with_a_host_tier(gpu):
+    w = _workload(12)
+    lens = W.fact_lengths(w)
+    budget = int(lens[:6].sum()) * L * H * D * 2 * 2
+    desc, keep = Hn.K.make_desc(L, H, D, synth.BF16, lens, 0, budget)
+    h = Hn.K.is_store_create(desc)
+    try:
+        with pytest.raises(Hn.K.ISError) as e:
+            Hn.K.is_store_append(h, np.array([2], np.int32), 0, 16, 16)
+        assert e.value.code == -9
+    finally:
+        Hn.K.is_store_destroy(h)
+    desc, keep = Hn.K.make_desc(L, H, D, synth.BF16, lens, 0, budget, spare_facts=1)
+    with pytest.raises(Hn.K.ISError) as e:
+        Hn.K.is_store_create(desc)
+    assert e.value.code == -9
