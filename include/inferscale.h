@@ -264,8 +264,8 @@ int is_retrieve_inject(const is_store* s, const uint16_t* q_f16, int32_t n_req, 
  *                      has an index, else NULL)
  *   first_id           host out: the id of the first new fact (ids are
  *                      consecutive)
- * The new facts go to HBM, into the spare room reserved at creation.
- * Asynchronous on `stream`: calls that use the new facts must be ordered
+ * The new facts go to HBM, into the spare room reserved at creation or the
+ * room that removed facts left (first fit).  Asynchronous on `stream`: calls that use the new facts must be ordered
  * after it on the device (same stream, or synchronized).  The sources must
  * stay valid until the stream has completed.
  * Errors: IS_ERR_INVALID_ARG, IS_ERR_ALIGN, IS_ERR_OOM (no spare room),
@@ -286,6 +286,24 @@ int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, int32_t win
  */
 int is_store_update(is_store* s, int64_t fact_id, int32_t window, const void* k_enc,
                     const void* v_enc, const uint16_t* emb, void* stream);
+
+/*
+ * Evicts facts from the store.  A personal memory store drops facts as
+ * well as gaining them; the pages define the store only by what it holds
+ * (Offline phase), so removal is the plain one: the listed facts leave the
+ * store, the others keep their order and are renumbered densely -- a
+ * fact's new id is its old id minus the number of removed ids below it.
+ *   ids[n]   host int32, distinct, each in [0, n_facts); n = 0 is a no-op
+ * The surviving facts' K/V stay where they are (their addresses move in the
+ * fact tables only); the removed facts' HBM spans are reused by later
+ * appends; the embedding index is compacted into a fresh arena.
+ * Synchronous: returns when the work queued on `stream` has completed.
+ * Must not overlap any other call that uses the store.
+ * Errors: IS_ERR_INVALID_ARG (null, an id listed twice), IS_ERR_FACT_ID,
+ * IS_ERR_UNSUPPORTED (the store has a host tier), IS_ERR_OOM, IS_ERR_HIP;
+ * nothing changes on error.
+ */
+int is_store_remove(is_store* s, int64_t n, const int32_t* ids, void* stream);
 
 /*
  * Query-only attention over the paged cache, the step that follows the

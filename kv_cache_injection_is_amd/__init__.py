@@ -26,7 +26,7 @@ IS_ROPE_NONE, IS_ROPE_LLAMA3 = 0, 1
 
 EXPORTS = ("is_store_create", "is_store_load", "is_store_get_info", "is_topk", "is_inject",
            "is_retrieve_inject", "is_attend", "is_store_append", "is_store_update",
-           "is_inject_check", "is_store_destroy", "is_last_error")
+           "is_store_remove", "is_inject_check", "is_store_destroy", "is_last_error")
 
 
 class ISError(RuntimeError):
@@ -89,6 +89,7 @@ def lib() -> ctypes.CDLL:
         L.is_store_append.argtypes = [P, c.c_int32, P, c.c_int32, P, P, P,
                                       c.POINTER(c.c_int64), P]
         L.is_store_update.argtypes = [P, c.c_int64, c.c_int32, P, P, P, P]
+        L.is_store_remove.argtypes = [P, c.c_int64, P, P]
         L.is_inject_check.argtypes = [c.POINTER(is_store_desc), c.c_int32, P, P, P, P,
                                       c.c_int32, c.POINTER(is_cache), c.POINTER(is_rope),
                                       c.POINTER(c.c_int64)]
@@ -225,6 +226,13 @@ def is_store_update(store: int, fact_id: int, window: int, k_enc, v_enc, emb=Non
                     stream=None) -> None:
     _check(lib().is_store_update(store, fact_id, window, _dev(k_enc), _dev(v_enc), _dev(emb),
                                  _stream(stream)))
+
+
+def is_store_remove(store: int, ids, stream=None) -> None:
+    """ids: host array of the fact ids to evict; the rest are renumbered
+    densely in their order.  Returns once the stream has completed."""
+    a, a_p = _host(ids, np.int32)
+    _check(lib().is_store_remove(store, len(a), a_p, _stream(stream)))
 
 
 def make_cache(k_base, v_base, strides, block_size, n_blocks, dtype) -> is_cache:

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -70,8 +71,14 @@ struct is_store {
   int64_t n_facts = 0, n_hbm = 0;
   int64_t max_facts = 0;          // facts the tables and the embedding arena hold
   int64_t hbm_tokens = 0;         // tokens the HBM arenas hold
+  int64_t hbm_next = 0;           // arena tokens below this are (or were) in use
+  std::map<int64_t, int64_t> free_spans;  // freed arena token spans: start -> length
   std::vector<int32_t> len;
-  std::vector<int64_t> tok_off;   // [n_facts + 1]
+  // [n_facts + 1]: token offsets of the facts laid back to back in id
+  // order (the layout of load sources; the host tier's layout too).  HBM
+  // facts need not sit in that order once facts are removed: their
+  // addresses are k_addr / v_addr.
+  std::vector<int64_t> tok_off;
   size_t es = 0;
   void* k_dev = nullptr;          // HBM arenas, facts [0, n_hbm)
   void* v_dev = nullptr;
@@ -111,16 +118,64 @@ struct is_store {
     return host[lo];
   }
   char* k_at(int64_t f) const {
-    if (f < n_hbm) return (char*)k_dev + fact_bytes(0, f);
+    if (f < n_hbm) return reinterpret_cast<char*>((uintptr_t)k_addr[(size_t)f]);
     const HostChunk& c = chunk_of(f);
     return (char*)c.k + fact_bytes(c.f0, f);
   }
   char* v_at(int64_t f) const {
-    if (f < n_hbm) return (char*)v_dev + fact_bytes(0, f);
+    if (f < n_hbm) return reinterpret_cast<char*>((uintptr_t)v_addr[(size_t)f]);
     const HostChunk& c = chunk_of(f);
     return (char*)c.v + fact_bytes(c.f0, f);
   }
+  size_t token_bytes() const { return (size_t)row_elems() * es; }
+  // Arena token offset of HBM fact f (K and V sit at the same offset).
+  int64_t arena_token(int64_t f) const {
+    return (int64_t)(((uintptr_t)k_addr[(size_t)f] - (uintptr_t)k_dev) / token_bytes());
+  }
 };
+
+namespace {
+
+// First fit in the freed spans, else the end of the used arena; -1 if
+// neither has `n` tokens.  Works on the caller's copies, so a batch of
+// allocations can be dropped as a whole.
+int64_t arena_alloc(std::map<int64_t, int64_t>& spans, int64_t& next, int64_t cap, int64_t n) {
+  for (auto it = spans.begin(); it != spans.end(); ++it) {
+    if (it->second < n) continue;
+    const int64_t at = it->first, rest = it->second - n;
+    spans.erase(it);
+    if (rest > 0) spans.emplace(at + n, rest);
+    return at;
+  }
+  if (next + n > cap) return -1;
+  next += n;
+  return next - n;
+}
+
+// Returns [at, at + n) to the free spans, merged with its neighbours; a
+// span that reaches the end of the used arena moves that end back.
+void arena_free(std::map<int64_t, int64_t>& spans, int64_t& next, int64_t at, int64_t n) {
+  auto hi = spans.lower_bound(at);
+  if (hi != spans.end() && hi->first == at + n) {
+    n += hi->second;
+    hi = spans.erase(hi);
+  }
+  if (hi != spans.begin()) {
+    auto lo = std::prev(hi);
+    if (lo->first + lo->second == at) {
+      at = lo->first;
+      n += lo->second;
+      spans.erase(lo);
+    }
+  }
+  if (at + n == next) {
+    next = at;
+    return;
+  }
+  spans.emplace(at, n);
+}
+
+}  // namespace
 
 namespace {
 
@@ -246,6 +301,7 @@ IS_EXPORT int is_store_create(const is_store_desc* d, is_store** out) {
   }
   s->max_facts = s->n_facts + std::max<int64_t>(d->spare_facts, 0);
   s->hbm_tokens = s->tok_off[s->n_hbm] + std::max<int64_t>(d->spare_tokens, 0);
+  s->hbm_next = s->tok_off[s->n_hbm];
   const size_t hbm_bytes = (size_t)s->hbm_tokens * s->row_elems() * s->es;
   if (hbm_bytes > 0 && (hipMalloc(&s->k_dev, hbm_bytes) != hipSuccess ||
                         hipMalloc(&s->v_dev, hbm_bytes) != hipSuccess)) {
@@ -349,9 +405,15 @@ IS_EXPORT int is_store_load(is_store* s, int64_t first, int64_t n, const void* k
   for (const Part& p : parts) {
     if (p.f1 <= p.f0) continue;
     const hipMemcpyKind kind = p.host ? from_dev_to_host : from_dev;
-    // HBM facts are one span; host facts are copied chunk by chunk.
+    // HBM facts are copied by runs that are contiguous in the arena (the
+    // whole range unless facts were removed), host facts chunk by chunk.
     for (int64_t f = p.f0; f < p.f1;) {
-      const int64_t g = p.host ? std::min(p.f1, s->chunk_of(f).f1) : p.f1;
+      int64_t g = f + 1;
+      if (p.host) {
+        g = std::min(p.f1, s->chunk_of(f).f1);
+      } else {
+        while (g < p.f1 && s->arena_token(g) == s->arena_token(g - 1) + s->len[(size_t)g - 1]) ++g;
+      }
       const size_t bytes = s->fact_bytes(f, g);
       hipError_t e;
       if (k && (e = hipMemcpy(s->k_at(f), (const char*)k + src_off, bytes, kind)) != hipSuccess)
@@ -802,26 +864,27 @@ IS_EXPORT int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, i
     return fail(IS_ERR_INVALID_ARG, "the store has an index: the new facts need embeddings");
   if (((uintptr_t)k_enc & 15u) || ((uintptr_t)v_enc & 15u) || ((uintptr_t)emb & 15u))
     return fail(IS_ERR_ALIGN, "encodings and embeddings must be 16-byte aligned");
-  int64_t tokens = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (fact_len[i] < 1) return fail(IS_ERR_INVALID_ARG, "fact lengths must be >= 1");
     if ((int64_t)window + fact_len[i] > ((int64_t)1 << 24))
       return fail(IS_ERR_INVALID_ARG, "window + fact length must stay below 2^24");
-    tokens += fact_len[i];
   }
   DeviceGuard guard(s->device);
   std::lock_guard<std::mutex> lock(s->mu);
   const int64_t f0 = s->n_facts;
-  if (f0 + n > s->max_facts || s->tok_off[f0] + tokens > s->hbm_tokens)
-    return fail(IS_ERR_OOM, "no spare room left in the store for these facts");
-  // new facts' blocks follow the last fact in the HBM arenas
+  if (f0 + n > s->max_facts) return fail(IS_ERR_OOM, "no spare fact slots left in the store");
+  // each new fact's block: first fit in the spans that removed facts left,
+  // else behind the used part of the HBM arenas
+  std::map<int64_t, int64_t> spans = s->free_spans;
+  int64_t next = s->hbm_next;
   std::vector<is::IngestItem> items((size_t)n);
   std::vector<int32_t> new_len(fact_len, fact_len + n);
   std::vector<uint64_t> new_k((size_t)n), new_v((size_t)n);
-  int64_t tok = s->tok_off[f0];
   size_t src = 0;
-  const size_t row = (size_t)s->row_elems() * s->es;   // one token over all layers and heads
+  const size_t row = s->token_bytes();   // one token over all layers and heads
   for (int32_t i = 0; i < n; ++i) {
+    const int64_t tok = arena_alloc(spans, next, s->hbm_tokens, fact_len[i]);
+    if (tok < 0) return fail(IS_ERR_OOM, "no spare room left in the store for these facts");
     is::IngestItem& it = items[(size_t)i];
     it.src_k = static_cast<const char*>(k_enc) + src;
     it.src_v = static_cast<const char*>(v_enc) + src;
@@ -832,7 +895,6 @@ IS_EXPORT int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, i
     new_k[(size_t)i] = (uint64_t)(uintptr_t)it.dst_k;
     new_v[(size_t)i] = (uint64_t)(uintptr_t)it.dst_v;
     src += (size_t)(window + fact_len[i]) * row;
-    tok += fact_len[i];
   }
   // the device fact tables' new entries travel with the work list
   const size_t tab_bytes = (size_t)n * (4 + 8 + 8);
@@ -866,6 +928,8 @@ IS_EXPORT int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, i
   }
   s->n_facts += n;
   s->n_hbm += n;
+  s->free_spans.swap(spans);
+  s->hbm_next = next;
   return IS_OK;
 }
 
@@ -880,11 +944,12 @@ IS_EXPORT int is_store_update(is_store* s, int64_t fact_id, int32_t window, cons
     return fail(IS_ERR_ALIGN, "encodings and embeddings must be 16-byte aligned");
   if (emb != nullptr && s->emb_dim == 0)
     return fail(IS_ERR_INVALID_ARG, "store has no embedding index");
+  DeviceGuard guard(s->device);
+  std::lock_guard<std::mutex> lock(s->mu);
+  if (fact_id >= s->n_facts) return fail(IS_ERR_FACT_ID, "fact id out of range");
   const int32_t len = s->len[(size_t)fact_id];
   if ((int64_t)window + len > ((int64_t)1 << 24))
     return fail(IS_ERR_INVALID_ARG, "window + fact length must stay below 2^24");
-  DeviceGuard guard(s->device);
-  std::lock_guard<std::mutex> lock(s->mu);
   std::vector<is::IngestItem> items(1);
   items[0].src_k = static_cast<const char*>(k_enc);
   items[0].src_v = static_cast<const char*>(v_enc);
@@ -902,5 +967,92 @@ IS_EXPORT int is_store_update(is_store* s, int64_t fact_id, int32_t window, cons
       (e = is::launch_emb_relayout(emb, fact_id, 1, s->emb_dim, s->emb, st)) != hipSuccess)
     return hip_fail(e, "embedding relayout");
   if ((e = hipEventRecord(sl->done, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return IS_OK;
+}
+
+IS_EXPORT int is_store_remove(is_store* s, int64_t n, const int32_t* ids, void* stream) {
+  is::clear_error();
+  if (s == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  if (n < 0) return fail(IS_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 0 && ids == nullptr) return fail(IS_ERR_INVALID_ARG, "null ids");
+  DeviceGuard guard(s->device);
+  std::lock_guard<std::mutex> lock(s->mu);
+  if (s->n_hbm < s->n_facts)
+    return fail(IS_ERR_UNSUPPORTED, "removal needs a store without a host tier");
+  std::vector<char> gone((size_t)s->n_facts, 0);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t f = ids[i];
+    if (f < 0 || (int64_t)f >= s->n_facts) return fail(IS_ERR_FACT_ID, "fact id out of range");
+    if (gone[(size_t)f]) return fail(IS_ERR_INVALID_ARG, "fact id listed twice");
+    gone[(size_t)f] = 1;
+  }
+  if (n == 0) return IS_OK;
+  // survivors in id order; their blocks stay where they are
+  const int64_t m = s->n_facts - n;
+  std::vector<int32_t> keep;
+  keep.reserve((size_t)m);
+  for (int64_t f = 0; f < s->n_facts; ++f)
+    if (!gone[(size_t)f]) keep.push_back((int32_t)f);
+  std::vector<int32_t> len((size_t)m);
+  std::vector<uint64_t> k_addr((size_t)m), v_addr((size_t)m);
+  for (int64_t i = 0; i < m; ++i) {
+    len[(size_t)i] = s->len[(size_t)keep[(size_t)i]];
+    k_addr[(size_t)i] = s->k_addr[(size_t)keep[(size_t)i]];
+    v_addr[(size_t)i] = s->v_addr[(size_t)keep[(size_t)i]];
+  }
+  // device work first: new fact tables, then the compacted index
+  const size_t tab_bytes = align256((size_t)m * 4) + (size_t)m * 16 + (size_t)m * 4;
+  Slot* sl = nullptr;
+  int rc = acquire_slot(s, std::max<size_t>(tab_bytes, 16), &sl);
+  if (rc != IS_OK) return rc;
+  char* h = static_cast<char*>(sl->host);
+  char* dv = static_cast<char*>(sl->dev);
+  const size_t o_k = align256((size_t)m * 4), o_v = o_k + (size_t)m * 8, o_keep = o_v + (size_t)m * 8;
+  std::memcpy(h, len.data(), (size_t)m * 4);
+  std::memcpy(h + o_k, k_addr.data(), (size_t)m * 8);
+  std::memcpy(h + o_v, v_addr.data(), (size_t)m * 8);
+  std::memcpy(h + o_keep, keep.data(), (size_t)m * 4);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  uint16_t* emb = nullptr;
+  if (m > 0) {
+    if ((e = hipMemcpyAsync(dv, h, tab_bytes, hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(s->d_len, dv, (size_t)m * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(s->d_k_addr, dv + o_k, (size_t)m * 8, hipMemcpyDeviceToDevice, st)) !=
+            hipSuccess ||
+        (e = hipMemcpyAsync(s->d_v_addr, dv + o_v, (size_t)m * 8, hipMemcpyDeviceToDevice, st)) !=
+            hipSuccess)
+      return hip_fail(e, "fact table update");
+  }
+  if (s->emb_dim > 0) {
+    const size_t bytes = s->emb_alloc_bytes();
+    if (hipMalloc((void**)&emb, bytes) != hipSuccess) return fail(IS_ERR_OOM, "embedding arena");
+    if ((e = hipMemsetAsync(emb, 0, bytes, st)) != hipSuccess ||
+        (e = is::launch_emb_compact(s->emb, reinterpret_cast<const int32_t*>(dv + o_keep), m,
+                                    s->emb_dim, emb, st)) != hipSuccess) {
+      (void)hipStreamSynchronize(st);
+      (void)hipFree(emb);
+      return hip_fail(e, "embedding compaction");
+    }
+  }
+  if ((e = hipEventRecord(sl->done, st)) != hipSuccess ||
+      (e = hipStreamSynchronize(st)) != hipSuccess) {
+    if (emb) (void)hipFree(emb);
+    return hip_fail(e, "removal");
+  }
+  // host state last: the removed facts' spans go back to the arena
+  for (int64_t f = 0; f < s->n_facts; ++f)
+    if (gone[(size_t)f]) arena_free(s->free_spans, s->hbm_next, s->arena_token(f), s->len[(size_t)f]);
+  if (emb) {
+    (void)hipFree(s->emb);
+    s->emb = emb;
+  }
+  s->len.swap(len);
+  s->k_addr.swap(k_addr);
+  s->v_addr.swap(v_addr);
+  s->tok_off.assign((size_t)m + 1, 0);
+  for (int64_t f = 0; f < m; ++f) s->tok_off[(size_t)f + 1] = s->tok_off[(size_t)f] + s->len[(size_t)f];
+  s->n_facts = m;
+  s->n_hbm = m;
   return IS_OK;
 }

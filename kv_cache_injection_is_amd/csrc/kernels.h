@@ -128,6 +128,11 @@ struct TopkLaunch {
 hipError_t launch_emb_relayout(const uint16_t* rows, int64_t first, int64_t n,
                                int32_t emb_dim, uint16_t* emb, hipStream_t stream);
 
+// Copies the blocked rows of facts keep[0..n) of `from` to rows 0..n of `to`
+// (both blocked, the same width); `to` must not overlap `from`.
+hipError_t launch_emb_compact(const uint16_t* from, const int32_t* keep, int64_t n,
+                              int32_t emb_dim, uint16_t* to, hipStream_t stream);
+
 // Facts in the threshold sample for a store of n_facts facts.
 int64_t topk_sample_size(int64_t n_facts);
 

@@ -486,6 +486,23 @@ __global__ __launch_bounds__(256) void emb_relayout(const uint16_t* __restrict__
   *reinterpret_cast<u32x4*>(emb + dst) = *reinterpret_cast<const u32x4*>(rows + r * emb_dim + p * 8);
 }
 
+// Moves the rows of facts keep[0..n) of the blocked layout `from` to rows
+// 0..n of `to`, all `padded_dim` columns (the padding stays zero).
+__global__ __launch_bounds__(256) void emb_compact(const uint16_t* __restrict__ from,
+                                                  const int32_t* __restrict__ keep, int64_t n,
+                                                  int32_t padded_dim, uint16_t* __restrict__ to) {
+  const int pieces = padded_dim / 8;
+  const int n_chunks = padded_dim / kKC;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * pieces) return;
+  const int64_t r = i / pieces;
+  const int p = (int)(i % pieces);
+  const int64_t f = keep[r];
+  const int64_t src = ((f / kFT * n_chunks + p / 8) * kFT + f % kFT) * kKC + (p % 8) * 8;
+  const int64_t dst = ((r / kFT * n_chunks + p / 8) * kFT + r % kFT) * kKC + (p % 8) * 8;
+  *reinterpret_cast<u32x4*>(to + dst) = *reinterpret_cast<const u32x4*>(from + src);
+}
+
 // Copies queries [n_q][emb_dim] to [n_q][padded_dim], zero-filling the tail.
 __global__ __launch_bounds__(256) void pad_queries(const uint16_t* __restrict__ q, int32_t n_q,
                                                   int32_t emb_dim, int32_t padded_dim,
@@ -505,6 +522,16 @@ hipError_t launch_emb_relayout(const uint16_t* rows, int64_t first, int64_t n, i
   const int64_t threads = n * (emb_dim / 8);
   hipLaunchKernelGGL(emb_relayout, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                      rows, first, n, emb_dim, topk_padded_dim(emb_dim), emb);
+  return hipGetLastError();
+}
+
+hipError_t launch_emb_compact(const uint16_t* from, const int32_t* keep, int64_t n,
+                              int32_t emb_dim, uint16_t* to, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int32_t padded = topk_padded_dim(emb_dim);
+  const int64_t threads = n * (padded / 8);
+  hipLaunchKernelGGL(emb_compact, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     from, keep, n, padded, to);
   return hipGetLastError();
 }
 

@@ -14,6 +14,13 @@ Personalized LLM Serving", gist.science explainer, technical summary):
   token_slots, inject  Online phase, scatter-copy into the paged KV cache
   topk                 Contributions, GPU-resident retrieval (exact
                        inner-product top-k stands in for the index)
+  attend               Online phase, query-only prefill over the cache that
+                       holds the injected facts (Theorem 6 end to end)
+  ingest               Offline phase, context-window encoding: only the
+                       fact's own tokens' K/V are kept
+  survivors            store maintenance (the pages define the store by what
+                       it holds; eviction is plain removal with the survivors
+                       renumbered in order)
 Every function is pinned by tests/test_oracle_pins.py against closed forms,
 invariants, library routines and brute force.
 """
@@ -211,3 +218,14 @@ def ingest(n_layers, n_heads, d, lens, window, enc) -> np.ndarray:
     lib().or_ingest(n_layers, n_heads, d, enc.itemsize, len(lens), _p(lens), window, _p(enc),
                     _p(out))
     return out
+
+
+def survivors(n_facts: int, removed) -> np.ndarray:
+    """Eviction of `removed` (distinct ids in [0, n_facts)) from a store of
+    n_facts facts: the old ids of the facts that stay, in id order, so that
+    entry i is the old id of new fact i."""
+    gone = [int(f) for f in removed]
+    if len(set(gone)) != len(gone) or any(f < 0 or f >= n_facts for f in gone):
+        raise ValueError("removed ids must be distinct and in range")
+    drop = set(gone)
+    return np.array([f for f in range(n_facts) if f not in drop], dtype=np.int32)

@@ -37,6 +37,9 @@ def test_null_arguments_are_rejected_without_gpu():
                                   None) == -1
     assert lib.is_attend(None, None, None, 1, 1, 1, None, None, None, None, None, 1, None,
                          None) == -1
+    assert lib.is_store_append(None, 1, None, 0, None, None, None, None, None) == -1
+    assert lib.is_store_update(None, 0, 0, None, None, None, None) == -1
+    assert lib.is_store_remove(None, 1, None, None) == -1
 
 
 def _desc(dtype=K.IS_DTYPE_BF16, head_dim=128, lens=(5, 7, 3, 9), emb_dim=0):

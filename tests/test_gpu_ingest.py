@@ -139,3 +139,115 @@ def test_append_rejected_with_a_host_tier(gpu):
     with pytest.raises(Hn.K.ISError) as e:
         Hn.K.is_store_create(desc)
     assert e.value.code == -9
+    desc, keep = Hn.K.make_desc(L, H, D, synth.BF16, lens, 0, budget)
+    h = Hn.K.is_store_create(desc)
+    try:
+        with pytest.raises(Hn.K.ISError) as e:
+            Hn.K.is_store_remove(h, [0])
+        assert e.value.code == -9
+    finally:
+        Hn.K.is_store_destroy(h)
+
+
+def _gen_rows(lens, old_ids, new_ids, tag_offset=0):
+    """fact -> (K, V) generator rows: new id `n` holds old fact `o`'s rows."""
+    row = L * H * D
+    return {int(n): (synth.fact_kv(SEED, synth.TAG_K, int(o) + tag_offset, int(lens[o]) * row,
+                                   synth.BF16),
+                     synth.fact_kv(SEED, synth.TAG_V, int(o) + tag_offset, int(lens[o]) * row,
+                                   synth.BF16))
+            for n, o in zip(new_ids, old_ids)}
+
+
+def test_remove_renumbers_and_appends_reuse_the_room(gpu):
+    """Eviction: the survivors are renumbered in order (the oracle's
+    survivors), top-k and inject see the compacted store, appends fill the
+    freed spans first fit (no spare tokens were reserved), and loads into
+    facts whose blocks are no longer contiguous land where inject reads."""
+    import torch
+    n0 = 30
+    w = _workload(n0)
+    lens = W.fact_lengths(w)
+    row = L * H * D
+    desc, keep_alive = Hn.K.make_desc(L, H, D, synth.BF16, lens, EMB, spare_facts=4)
+    h = Hn.K.is_store_create(desc)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    try:
+        emb = synth.embeddings(SEED, 0, n0, EMB)
+        Hn.K.is_store_load(h, 0, n0, synth.kv_range(SEED, synth.TAG_K, 0, lens, row, synth.BF16),
+                           synth.kv_range(SEED, synth.TAG_V, 0, lens, row, synth.BF16), emb)
+        removed = [0, 7, 8, 29, 15]
+        Hn.log(f"remove {removed} of {n0}")
+        Hn.K.is_store_remove(h, removed)
+        keep = oracle.survivors(n0, removed)
+        info = Hn.K.is_store_get_info(h)
+        assert info.n_facts == len(keep) == 25
+        assert info.total_tokens == int(lens[keep].sum())
+        lens_now = lens[keep].astype(np.int32)
+        st = Hn.Store(w, lens_now, None, h, None)
+        q = synth.queries(SEED + 1, 12, EMB)
+        ids, sc = Hn.gpu_topk(st, q, 10)
+        Hn.check_topk(q, emb[keep], ids, sc, 10)
+        got, _ = Hn.gpu_topk(st, emb[keep[[0, 6, 24]]], 1)
+        assert got[:, 0].tolist() == [0, 6, 24]
+        rows = _gen_rows(lens, keep, range(len(keep)))
+        _inject_and_check(st, w, Hn.make_cache(w), lens_now, [0, 6, 24, 5, 13, 20], rows)
+        # the freed spans, in arena order: fact 0's, facts 7-8 merged, fact
+        # 15's; fact 29's was the arena's end.  Exact fits, first fit.
+        new_lens = np.array([lens[0], lens[7] + lens[8], lens[15], lens[29]], np.int32)
+        ent = np.arange(400, 404)
+        k_enc, _ = _encodings(ent, new_lens, 3, synth.TAG_K)
+        v_enc, _ = _encodings(ent, new_lens, 3, synth.TAG_V)
+        Hn.log(f"append {list(new_lens)} into the freed room")
+        first = Hn.K.is_store_append(h, new_lens, 3, dev(k_enc), dev(v_enc),
+                                     dev(synth.embeddings(SEED, 400, 4, EMB)))
+        torch.cuda.synchronize()
+        assert first == 25
+        k_ora = oracle.ingest(L, H, D, new_lens, 3, k_enc)
+        v_ora = oracle.ingest(L, H, D, new_lens, 3, v_enc)
+        cut = np.concatenate([[0], np.cumsum(new_lens)]) * row
+        for i in range(4):
+            rows[25 + i] = (k_ora[cut[i]:cut[i + 1]], v_ora[cut[i]:cut[i + 1]])
+        lens_now = np.concatenate([lens_now, new_lens]).astype(np.int32)
+        st = Hn.Store(w, lens_now, None, h, None)
+        _inject_and_check(st, w, Hn.make_cache(w), lens_now, [26, 5, 25, 28, 6, 27, 0], rows)
+        got, _ = Hn.gpu_topk(st, synth.embeddings(SEED, 400, 4, EMB), 1)
+        assert got[:, 0].tolist() == [25, 26, 27, 28]
+        # the arena is full now
+        with pytest.raises(Hn.K.ISError) as e:
+            one = np.array([1], np.int32)
+            Hn.K.is_store_append(h, one, 0, dev(np.zeros(row, np.uint16)),
+                                 dev(np.zeros(row, np.uint16)), dev(np.zeros(EMB, np.uint16)))
+        assert e.value.code == -7
+        # new values for facts 4..9 (old 5, 6, 9, 10, 11, 12): their blocks
+        # are no longer one span
+        sub = np.arange(4, 10)
+        k_h = np.concatenate([synth.fact_kv(SEED, synth.TAG_K, 900 + int(f), int(lens_now[f]) * row,
+                                            synth.BF16) for f in sub])
+        v_h = np.concatenate([synth.fact_kv(SEED, synth.TAG_V, 900 + int(f), int(lens_now[f]) * row,
+                                            synth.BF16) for f in sub])
+        Hn.K.is_store_load(h, 4, 6, k_h, v_h)
+        cut = np.concatenate([[0], np.cumsum(lens_now[sub])]) * row
+        for i, f in enumerate(sub):
+            rows[int(f)] = (k_h[cut[i]:cut[i + 1]], v_h[cut[i]:cut[i + 1]])
+        _inject_and_check(st, w, Hn.make_cache(w), lens_now, [9, 4, 26, 5, 7, 8, 6], rows)
+        # refusals change nothing
+        for bad, code in (([3, 3], -1), ([29], -2), ([-1], -2)):
+            with pytest.raises(Hn.K.ISError) as e:
+                Hn.K.is_store_remove(h, bad)
+            assert e.value.code == code
+        assert Hn.K.is_store_get_info(h).n_facts == 29
+        # everything out, then one fact back in
+        Hn.K.is_store_remove(h, np.arange(29))
+        assert Hn.K.is_store_get_info(h).n_facts == 0
+        with pytest.raises(Hn.K.ISError):
+            Hn.gpu_topk(st, q[:1], 1)
+        k_enc, _ = _encodings([500], [20], 0, synth.TAG_K)
+        assert Hn.K.is_store_append(h, np.array([20], np.int32), 0, dev(k_enc), dev(k_enc),
+                                    dev(synth.embeddings(SEED, 500, 1, EMB))) == 0
+        torch.cuda.synchronize()
+        st = Hn.Store(w, np.array([20], np.int32), None, h, None)
+        got, _ = Hn.gpu_topk(st, synth.embeddings(SEED, 500, 1, EMB), 1)
+        assert got[0, 0] == 0
+    finally:
+        Hn.K.is_store_destroy(h)

@@ -613,3 +613,27 @@ def test_ingest_without_window_is_the_identity():
     lens = np.array([3, 7], np.int32)
     enc = synth.fact_kv(22, synth.TAG_K, 0, int(lens.sum()) * L * H * d, synth.BF16)
     assert np.array_equal(oracle.ingest(L, H, d, lens, 0, enc), enc)
+
+
+# ----------------------------------------------------------------- eviction
+
+def test_survivors_renumbering_closed_form():
+    """New id of a kept fact = old id minus the number of removed ids below
+    it; nothing removed survives; every kept fact appears once."""
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 17, 300):
+        removed = rng.choice(n, size=rng.integers(0, n + 1), replace=False)
+        keep = oracle.survivors(n, removed)
+        assert len(keep) == n - len(removed)
+        assert not set(keep.tolist()) & set(removed.tolist())
+        for new, old in enumerate(keep):
+            assert new == old - int((removed < old).sum())
+
+
+def test_survivors_special_cases():
+    assert oracle.survivors(5, []).tolist() == [0, 1, 2, 3, 4]
+    assert oracle.survivors(5, [4, 0]).tolist() == [1, 2, 3]
+    assert oracle.survivors(3, [2, 1, 0]).tolist() == []
+    for bad in ([1, 1], [5], [-1]):
+        with pytest.raises(ValueError):
+            oracle.survivors(5, bad)
