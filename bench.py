@@ -294,6 +294,56 @@ def host_tier_latency(torch, K, W, Hn, reps: int) -> dict:
             if t_mixed > t_hbm else None}
 
 
+def ingest_rate(torch, K, W, synth, reps: int, n_batch: int = 512, window: int = 32) -> dict:
+    """Store ingest on the Mistral-7B geometry: appends of n_batch facts
+    (the workload's lognormal lengths) packed from context-window encodings
+    (`window` tokens before each fact) into spare HBM room.  Each append is
+    timed with HIP events on its stream; algorithmic bytes = the new facts'
+    K and V read once from the encodings and written once into the store."""
+    w = W.WORKLOADS["mistral7b_batch"]
+    lens = W.fact_lengths(w)[:n_batch].astype(np.int32)
+    row = w.row_elems
+    stream = torch.cuda.current_stream()
+    tokens = int(lens.sum())
+    rounds = reps + 1
+    desc, keep = K.make_desc(w.n_layers, w.n_kv_heads, w.head_dim, w.dtype, lens[:1], w.emb_dim,
+                             spare_facts=n_batch * rounds, spare_tokens=tokens * rounds)
+    h = K.is_store_create(desc)
+    try:
+        enc_rows = (window + lens).astype(np.int64) * row
+        off = np.zeros(n_batch + 1, np.int64)
+        np.cumsum(enc_rows, out=off[1:])
+        d_off = torch.from_numpy(off).cuda()
+        k_enc = torch.empty(int(off[-1]) * w.elem_size, dtype=torch.uint8, device="cuda")
+        v_enc = torch.empty_like(k_enc)
+        synth.gpu_fill_kv(w.seed, synth.TAG_K, 0, d_off, int(off[-1]), w.dtype, k_enc.data_ptr(),
+                          stream.cuda_stream)
+        synth.gpu_fill_kv(w.seed, synth.TAG_V, 0, d_off, int(off[-1]), w.dtype, v_enc.data_ptr(),
+                          stream.cuda_stream)
+        emb = torch.from_numpy(synth.embeddings(w.seed, 0, n_batch, w.emb_dim).view(np.int16)).cuda()
+        K.is_store_append(h, lens, window, k_enc, v_enc, emb, stream)      # warm-up
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            K.is_store_append(h, lens, window, k_enc, v_enc, emb, stream)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        del k_enc, v_enc, emb
+    finally:
+        K.is_store_destroy(h)
+        torch.cuda.empty_cache()
+    alg = 2 * 2 * tokens * w.token_bytes
+    gbps = alg / (ms / 1e3) / 1e9
+    return {"workload": f"{n_batch} facts ({tokens} tokens, Mistral-7B geometry) appended from "
+                        f"encodings with a {window}-token window",
+            "ms": round(ms, 4), "GBps": round(gbps, 1),
+            "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg,
+            "facts_per_s": round(n_batch / (ms / 1e3), 1)}
+
+
 def copy_bandwidth(torch, gib: float = 4.0, reps: int = 5) -> float:
     """Plain device copy (read + write) in GB/s."""
     n = int(gib * (1 << 30))
@@ -377,6 +427,10 @@ def main() -> int:
                     help="leave out the top-k over 1M x 1024 embeddings")
     ap.add_argument("--skip-host-tier", action="store_true",
                     help="leave out the single-request host-tier latency")
+    ap.add_argument("--skip-ingest", action="store_true",
+                    help="leave out the store-ingest (append) rate")
+    ap.add_argument("--ingest-only", action="store_true",
+                    help="only run the store-ingest rate (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the path on a single MI355X; "
@@ -397,6 +451,10 @@ def main() -> int:
     from synth import workloads as W
     from tests import harness as Hn
 
+    if args.ingest_only:
+        print(json.dumps({"ingest": ingest_rate(torch, K, W, synth, max(args.steps, 3))}),
+              flush=True)
+        return 0
     if args.topk_1m_only:
         stream = torch.cuda.current_stream()
         flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -526,6 +584,11 @@ def main() -> int:
         except Exception as e:     # a box that cannot pin the tier
             host_tier = {"error": f"{type(e).__name__}: {e}"}
             log(f"host tier skipped: {host_tier['error']}")
+    ingest = None
+    if not args.skip_ingest:
+        log("store ingest: appends from window encodings")
+        ingest = ingest_rate(torch, K, W, synth, max(args.steps, 5))
+        log(f"ingest: {ingest['ms']:.3f} ms per append, {ingest['GBps']:.0f} GB/s")
     topk_1m = None
     if not args.skip_topk_1m:
         log("top-k over 1M x 1024 embeddings")
@@ -579,6 +642,7 @@ def main() -> int:
         "device_path": dev,
         "attend": attend,
         "host_tier": host_tier,
+        "ingest": ingest,
         "copy_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
     }

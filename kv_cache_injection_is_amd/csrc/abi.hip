@@ -818,6 +818,12 @@ IS_EXPORT int is_attend(const is_store* cs, const is_cache* cache, const is_rope
 
 namespace {
 
+// 16-byte pieces in one layer of a fact of `len` tokens (the packing kernel
+// indexes them in 32 bits).
+int64_t layer_pieces(const is_store* s, int64_t len) {
+  return (int64_t)s->H * len * s->d * (int64_t)s->es / 16;
+}
+
 // Stages `items` and launches the packing copy, 65535 facts per launch.
 int launch_ingest_items(is_store* s, const std::vector<is::IngestItem>& items, size_t extra_bytes,
                         const void* extra, hipStream_t st, Slot** out_slot, char** extra_dev) {
@@ -868,6 +874,8 @@ IS_EXPORT int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, i
     if (fact_len[i] < 1) return fail(IS_ERR_INVALID_ARG, "fact lengths must be >= 1");
     if ((int64_t)window + fact_len[i] > ((int64_t)1 << 24))
       return fail(IS_ERR_INVALID_ARG, "window + fact length must stay below 2^24");
+    if (layer_pieces(s, fact_len[i]) >= ((int64_t)1 << 31))
+      return fail(IS_ERR_INVALID_ARG, "a fact's layer must stay below 2^35 bytes");
   }
   DeviceGuard guard(s->device);
   std::lock_guard<std::mutex> lock(s->mu);
@@ -950,6 +958,8 @@ IS_EXPORT int is_store_update(is_store* s, int64_t fact_id, int32_t window, cons
   const int32_t len = s->len[(size_t)fact_id];
   if ((int64_t)window + len > ((int64_t)1 << 24))
     return fail(IS_ERR_INVALID_ARG, "window + fact length must stay below 2^24");
+  if (layer_pieces(s, len) >= ((int64_t)1 << 31))
+    return fail(IS_ERR_INVALID_ARG, "a fact's layer must stay below 2^35 bytes");
   std::vector<is::IngestItem> items(1);
   items[0].src_k = static_cast<const char*>(k_enc);
   items[0].src_v = static_cast<const char*>(v_enc);

@@ -8,37 +8,85 @@
 // [layer][kv_head][len][head_dim], rows window .. window + len - 1 of each
 // (layer, kv_head), bit for bit.
 //
-// One workgroup per (fact, layer): for that layer the fact's kv_heads are
-// len-row spans in both tensors, so the copy runs in 16-byte pieces over
-// the layer's H * len rows, K and V together.  Non-temporal accesses: the
-// data is neither read again soon nor written back to.
+// A pure copy, HBM-bound: each stored byte is read once and written once.
+// One workgroup per (fact, layer): that layer's kv_heads are H spans of len
+// rows in both tensors, so the workgroup walks the layer's H * len * row
+// bytes in 16-byte pieces, K and V together, U pieces of each per thread
+// loaded before any is stored (several loads in flight per lane hide the
+// HBM latency; the layer is short, so there is no second sweep to overlap
+// with).  Piece -> (head, offset) by 32-bit division: a layer of one fact
+// holds far fewer than 2^32 pieces.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+
+#ifndef IS_INGEST_U
+#define IS_INGEST_U 8          // pieces of K (and of V) in flight per thread
+#endif
+#ifndef IS_INGEST_NT
+#define IS_INGEST_NT 1         // non-temporal loads and stores
+#endif
+#ifndef IS_INGEST_THREADS
+#define IS_INGEST_THREADS 512
+#endif
 
 namespace is {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = IS_INGEST_THREADS;
+constexpr int kU = IS_INGEST_U;
+
+__device__ __forceinline__ u32x4 ld(const char* p) {
+#if IS_INGEST_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
+
+__device__ __forceinline__ void st(char* p, u32x4 v) {
+#if IS_INGEST_NT
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+#else
+  *reinterpret_cast<u32x4*>(p) = v;
+#endif
+}
 
 __global__ __launch_bounds__(kThreads) void ingest_kernel(IngestLaunch a) {
   const IngestItem it = a.items[blockIdx.y];
   const int layer = blockIdx.x;
-  const int64_t row = a.row_bytes;
-  const int64_t per_head = (int64_t)it.len * row / 16;      // 16-byte pieces per head span
-  const int64_t n = per_head * a.n_heads;
-  const int64_t src_rows = (int64_t)it.window + it.len;
-  for (int64_t c = threadIdx.x; c < n; c += kThreads) {
-    const int64_t hd = c / per_head, off = (c % per_head) * 16;
-    const int64_t lh = (int64_t)layer * a.n_heads + hd;
-    const int64_t s = (lh * src_rows + it.window) * row + off;
-    const int64_t d = lh * it.len * row + off;
-    const u32x4 kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(it.src_k + s));
-    const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(it.src_v + s));
-    __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(it.dst_k + d));
-    __builtin_nontemporal_store(vv, reinterpret_cast<u32x4*>(it.dst_v + d));
+  const uint32_t per_head = (uint32_t)it.len * (uint32_t)(a.row_bytes / 16);
+  const uint32_t n = per_head * (uint32_t)a.n_heads;
+  const int64_t src_head = ((int64_t)it.window + it.len) * a.row_bytes;   // bytes per source span
+  const int64_t dst_head = (int64_t)it.len * a.row_bytes;
+  const int64_t lh0 = (int64_t)layer * a.n_heads;
+  const char* __restrict__ sk = it.src_k + lh0 * src_head + (int64_t)it.window * a.row_bytes;
+  const char* __restrict__ sv = it.src_v + lh0 * src_head + (int64_t)it.window * a.row_bytes;
+  char* __restrict__ dk = it.dst_k + lh0 * dst_head;
+  char* __restrict__ dv = it.dst_v + lh0 * dst_head;
+  for (uint32_t c0 = threadIdx.x; c0 < n; c0 += kU * kThreads) {
+    u32x4 kv[kU], vv[kU];
+    int64_t so[kU], doff[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t c = c0 + (uint32_t)(u * kThreads);
+      const uint32_t h = c / per_head, q = c - h * per_head;
+      so[u] = h * src_head + (int64_t)q * 16;
+      doff[u] = h * dst_head + (int64_t)q * 16;
+      if (c < n) {
+        kv[u] = ld(sk + so[u]);
+        vv[u] = ld(sv + so[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (c0 + (uint32_t)(u * kThreads) < n) {
+        st(dk + doff[u], kv[u]);
+        st(dv + doff[u], vv[u]);
+      }
+    }
   }
 }
 
