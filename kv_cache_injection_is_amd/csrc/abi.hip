@@ -10,6 +10,7 @@
 
 #include "inferscale.h"
 #include "kernels.h"
+#include "arena.h"
 #include "plan.h"
 
 #define IS_EXPORT extern "C" __attribute__((visibility("default")))
@@ -72,7 +73,7 @@ struct is_store {
   int64_t max_facts = 0;          // facts the tables and the embedding arena hold
   int64_t hbm_tokens = 0;         // tokens the HBM arenas hold
   int64_t hbm_next = 0;           // arena tokens below this are (or were) in use
-  std::map<int64_t, int64_t> free_spans;  // freed arena token spans: start -> length
+  is::FreeSpans free_spans;       // freed arena token spans: start -> length
   std::vector<int32_t> len;
   // [n_facts + 1]: token offsets of the facts laid back to back in id
   // order (the layout of load sources; the host tier's layout too).  HBM
@@ -134,48 +135,7 @@ struct is_store {
   }
 };
 
-namespace {
 
-// First fit in the freed spans, else the end of the used arena; -1 if
-// neither has `n` tokens.  Works on the caller's copies, so a batch of
-// allocations can be dropped as a whole.
-int64_t arena_alloc(std::map<int64_t, int64_t>& spans, int64_t& next, int64_t cap, int64_t n) {
-  for (auto it = spans.begin(); it != spans.end(); ++it) {
-    if (it->second < n) continue;
-    const int64_t at = it->first, rest = it->second - n;
-    spans.erase(it);
-    if (rest > 0) spans.emplace(at + n, rest);
-    return at;
-  }
-  if (next + n > cap) return -1;
-  next += n;
-  return next - n;
-}
-
-// Returns [at, at + n) to the free spans, merged with its neighbours; a
-// span that reaches the end of the used arena moves that end back.
-void arena_free(std::map<int64_t, int64_t>& spans, int64_t& next, int64_t at, int64_t n) {
-  auto hi = spans.lower_bound(at);
-  if (hi != spans.end() && hi->first == at + n) {
-    n += hi->second;
-    hi = spans.erase(hi);
-  }
-  if (hi != spans.begin()) {
-    auto lo = std::prev(hi);
-    if (lo->first + lo->second == at) {
-      at = lo->first;
-      n += lo->second;
-      spans.erase(lo);
-    }
-  }
-  if (at + n == next) {
-    next = at;
-    return;
-  }
-  spans.emplace(at, n);
-}
-
-}  // namespace
 
 namespace {
 
@@ -883,7 +843,7 @@ IS_EXPORT int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, i
   if (f0 + n > s->max_facts) return fail(IS_ERR_OOM, "no spare fact slots left in the store");
   // each new fact's block: first fit in the spans that removed facts left,
   // else behind the used part of the HBM arenas
-  std::map<int64_t, int64_t> spans = s->free_spans;
+  is::FreeSpans spans = s->free_spans;
   int64_t next = s->hbm_next;
   std::vector<is::IngestItem> items((size_t)n);
   std::vector<int32_t> new_len(fact_len, fact_len + n);
@@ -891,7 +851,7 @@ IS_EXPORT int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, i
   size_t src = 0;
   const size_t row = s->token_bytes();   // one token over all layers and heads
   for (int32_t i = 0; i < n; ++i) {
-    const int64_t tok = arena_alloc(spans, next, s->hbm_tokens, fact_len[i]);
+    const int64_t tok = is::arena_alloc(spans, next, s->hbm_tokens, fact_len[i]);
     if (tok < 0) return fail(IS_ERR_OOM, "no spare room left in the store for these facts");
     is::IngestItem& it = items[(size_t)i];
     it.src_k = static_cast<const char*>(k_enc) + src;
@@ -1052,7 +1012,7 @@ IS_EXPORT int is_store_remove(is_store* s, int64_t n, const int32_t* ids, void* 
   }
   // host state last: the removed facts' spans go back to the arena
   for (int64_t f = 0; f < s->n_facts; ++f)
-    if (gone[(size_t)f]) arena_free(s->free_spans, s->hbm_next, s->arena_token(f), s->len[(size_t)f]);
+    if (gone[(size_t)f]) is::arena_free(s->free_spans, s->hbm_next, s->arena_token(f), s->len[(size_t)f]);
   if (emb) {
     (void)hipFree(s->emb);
     s->emb = emb;
