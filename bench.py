@@ -162,10 +162,30 @@ def device_path(torch, K, st, w, q, stream, cdesc, rope, prefix, bt, tokens, rep
         toks = int(st.lens[ids_h[0, :kk].numpy()].sum())
         lat[f"k{kk}"] = {"tokens": toks, "host_path_ms": round(t_host, 4),
                          "device_path_ms": round(t_dev, 4)}
+        # the same call captured once in a HIP graph and replayed
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                K.is_retrieve_inject(st.handle, q[:1], 1, kk, d_prefix[:1], d_bt[:1], cdesc, rope,
+                                     status, None, side)
+            torch.cuda.synchronize()
+
+            def replay():
+                graph.replay()
+                torch.cuda.synchronize()
+
+            lat[f"k{kk}"]["graph_replay_ms"] = round(median_ms(torch, replay, reps), 4)
+            assert int(status.item()) == 0, "device-side validation failed"
+            del graph
+        except Exception as e:          # report, keep the rest of the line
+            lat[f"k{kk}"]["graph_replay_ms"] = f"{type(e).__name__}: {e}"
     return {"step_ms": round(step, 4), "tokens_per_s": round(tokens / (step / 1e3), 1),
             "latency_one_request": lat,
             "note": "is_retrieve_inject: top-k, composition, validation and inject on the "
-                    "device; median wall time per call including the final synchronize"}
+                    "device; median wall time per call including the final synchronize; "
+                    "graph_replay_ms: the same call captured once in a HIP graph, replayed"}
 
 
 def attend_rate(torch, K, synth, st, w, cdesc, rope, prefix, seg_tokens, bt, stream,

@@ -241,6 +241,18 @@ int is_inject(const is_store* s, int32_t n_req, const int32_t* req_off,
  * enqueue nothing.  Requires 1 <= k <= min(64, n_facts), an embedding
  * index, and a cache of at most 2^32 slots (the slot check keeps a
  * bitmap of slots / 8 bytes).
+ * HIP graph capture: the call only launches kernels, so it may be captured
+ * on `stream` and the graph replayed (new query contents in the same
+ * buffers give new retrievals).  Captured calls use one scratch workspace
+ * per store, sized by the eager calls until the first capture and fixed
+ * from then on: capture after an eager call of at least the same n_req, k
+ * and cache (else IS_ERR_UNSUPPORTED, nothing captured).  Replays of
+ * graphs captured on one store share that workspace, so they must be
+ * ordered among themselves (one stream, or synchronized); eager calls use
+ * other scratch and may interleave.  A graph keeps the store as it was at
+ * capture (facts appended later are not searched); once a graph has been
+ * captured, is_store_remove refuses (it would free the index the graph
+ * reads).
  * Errors: IS_ERR_INVALID_ARG, IS_ERR_UNSUPPORTED, IS_ERR_DTYPE,
  * IS_ERR_ALIGN, IS_ERR_OOM, IS_ERR_HIP.
  */
@@ -300,7 +312,8 @@ int is_store_update(is_store* s, int64_t fact_id, int32_t window, const void* k_
  * Synchronous: returns when the work queued on `stream` has completed.
  * Must not overlap any other call that uses the store.
  * Errors: IS_ERR_INVALID_ARG (null, an id listed twice), IS_ERR_FACT_ID,
- * IS_ERR_UNSUPPORTED (the store has a host tier), IS_ERR_OOM, IS_ERR_HIP;
+ * IS_ERR_UNSUPPORTED (the store has a host tier, or a HIP graph was
+ * captured on it), IS_ERR_OOM, IS_ERR_HIP;
  * nothing changes on error.
  */
 int is_store_remove(is_store* s, int64_t n, const int32_t* ids, void* stream);

@@ -95,6 +95,12 @@ struct is_store {
   Slot slots[kSlots];              // inject staging (device + pinned host)
   int next_slot = 0;
   Slot topk_slots[kTopkSlots];     // top-k scratch (device only)
+  // Scratch of captured is_retrieve_inject calls: a graph replays with the
+  // addresses it captured, so those calls never take a ring slot (whose
+  // reuse is ordered by events that a graph cannot record); eager calls
+  // size it until the first capture; from then on it never moves.
+  Slot graph_slot;
+  bool captured = false;          // a graph holds addresses of this store
   int next_topk_slot = 0;
 
   int64_t row_elems() const { return (int64_t)L * H * d; }
@@ -152,6 +158,7 @@ void free_store(is_store* s) {
       if (sl.done) (void)hipEventDestroy(sl.done);
     }
   }
+  if (s->graph_slot.dev) (void)hipFree(s->graph_slot.dev);
   if (s->k_dev) (void)hipFree(s->k_dev);
   if (s->v_dev) (void)hipFree(s->v_dev);
   for (HostChunk& c : s->host) {
@@ -610,13 +617,34 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   const size_t off_g = off_buckets + (sort ? align256(2 * is::kComposeBuckets * sizeof(uint32_t)) : 0);
   const size_t off_bits = off_g + align256((size_t)n_pairs * 8);
   const size_t total = off_bits + align256((size_t)slot_words * 8);
+  // Under stream capture: the graph workspace, no events, no allocation.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &capture);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  const bool capturing = capture != hipStreamCaptureStatusNone;
   Slot* sl = nullptr;
-  rc = acquire_topk_slot(s, total, &sl);
-  if (rc != IS_OK) return rc;
+  if (capturing) {
+    if (s->graph_slot.cap < total)
+      return fail(IS_ERR_UNSUPPORTED,
+                  "capture needs an earlier eager call of at least this size on the store "
+                  "(it sizes the workspace that graph replays use)");
+    sl = &s->graph_slot;
+    s->captured = true;
+  } else {
+    rc = acquire_topk_slot(s, total, &sl);
+    if (rc != IS_OK) return rc;
+    Slot& gs = s->graph_slot;
+    if (!s->captured && gs.cap < total) {
+      if (gs.dev) (void)hipFree(gs.dev);
+      gs.dev = nullptr;
+      gs.cap = 0;
+      if (hipMalloc(&gs.dev, total) != hipSuccess) return fail(IS_ERR_OOM, "graph workspace");
+      gs.cap = total;
+    }
+  }
   char* p = static_cast<char*>(sl->dev);
   int32_t* ids = ids_out ? ids_out : reinterpret_cast<int32_t*>(p + off_ids);
   float* scores = reinterpret_cast<float*>(p + off_scores);
-  hipError_t e = hipSuccess;
   for (int32_t q0 = 0; q0 < n_req; q0 += 128) {
     is::TopkLaunch a{};
     a.emb = s->emb;
@@ -678,7 +706,8 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   a.lanes = is::inject_lanes(s->d, s->dtype);
   a.status = status;
   if ((e = is::launch_inject(a, st)) != hipSuccess) return hip_fail(e, "inject launch");
-  if ((e = hipEventRecord(sl->done, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (!capturing && (e = hipEventRecord(sl->done, st)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
   return IS_OK;
 }
 
@@ -949,6 +978,9 @@ IS_EXPORT int is_store_remove(is_store* s, int64_t n, const int32_t* ids, void* 
   std::lock_guard<std::mutex> lock(s->mu);
   if (s->n_hbm < s->n_facts)
     return fail(IS_ERR_UNSUPPORTED, "removal needs a store without a host tier");
+  if (s->captured)
+    return fail(IS_ERR_UNSUPPORTED,
+                "graphs were captured on this store: removal would free memory they read");
   std::vector<char> gone((size_t)s->n_facts, 0);
   for (int64_t i = 0; i < n; ++i) {
     const int32_t f = ids[i];
