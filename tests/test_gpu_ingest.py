@@ -123,6 +123,50 @@ def test_append_update_and_retrieve(gpu):
         Hn.K.is_store_destroy(h)
 
 
+def test_append_fp32_head64(gpu):
+    """The packing is dtype-blind (rows of head_dim x element size bytes): an
+    fp32 store with head_dim 64 (256-byte rows) and 3 kv heads, facts
+    appended behind a window of 5, injected and checked against the oracle
+    (fp32 K within 1e-5)."""
+    import torch
+    Lf, Hf, Df, win = 3, 3, 64, 5
+    w = W.WORKLOADS["llama8b_batch"].scaled(name="ingest32", n_layers=Lf, n_kv_heads=Hf,
+                                            head_dim=Df, dtype=synth.F32, n_facts=6,
+                                            emb_dim=0, block_size=16, n_blocks=64, seed=SEED,
+                                            scaling="none", theta=10000.0)
+    lens = W.fact_lengths(w)
+    row = Lf * Hf * Df
+    desc, keep = Hn.K.make_desc(Lf, Hf, Df, synth.F32, lens, 0, spare_facts=3, spare_tokens=200)
+    h = Hn.K.is_store_create(desc)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    try:
+        Hn.K.is_store_load(h, 0, 6, synth.kv_range(SEED, synth.TAG_K, 0, lens, row, synth.F32),
+                           synth.kv_range(SEED, synth.TAG_V, 0, lens, row, synth.F32))
+        new_lens = np.array([1, 30, 7], np.int32)
+        encs = {}
+        for tag in (synth.TAG_K, synth.TAG_V):
+            parts = []
+            for e, n in zip((700, 701, 702), new_lens):
+                fact = synth.fact_kv(SEED, tag, e, Lf * Hf * int(n) * Df, synth.F32)
+                pre = synth.fact_kv(SEED, tag, 60_000 + e, Lf * Hf * win * Df, synth.F32)
+                parts.append(np.concatenate([pre.reshape(Lf, Hf, win, Df),
+                                             fact.reshape(Lf, Hf, n, Df)], axis=2).reshape(-1))
+            encs[tag] = np.concatenate(parts)
+        first = Hn.K.is_store_append(h, new_lens, win, dev(encs[synth.TAG_K]),
+                                     dev(encs[synth.TAG_V]))
+        torch.cuda.synchronize()
+        assert first == 6
+        k_ora = oracle.ingest(Lf, Hf, Df, new_lens, win, encs[synth.TAG_K])
+        v_ora = oracle.ingest(Lf, Hf, Df, new_lens, win, encs[synth.TAG_V])
+        cut = np.concatenate([[0], np.cumsum(new_lens)]) * row
+        rows = {6 + i: (k_ora[cut[i]:cut[i + 1]], v_ora[cut[i]:cut[i + 1]]) for i in range(3)}
+        lens_all = np.concatenate([lens, new_lens]).astype(np.int32)
+        st = Hn.Store(w, lens_all, None, h, None)
+        _inject_and_check(st, w, Hn.make_cache(w), lens_all, [7, 2, 8, 6], rows)
+    finally:
+        Hn.K.is_store_destroy(h)
+
+
 def test_append_rejected_with_a_host_tier(gpu):
     w = _workload(12)
     lens = W.fact_lengths(w)
