@@ -249,10 +249,10 @@ int is_inject(const is_store* s, int32_t n_req, const int32_t* req_off,
  * and cache (else IS_ERR_UNSUPPORTED, nothing captured).  Replays of
  * graphs captured on one store share that workspace, so they must be
  * ordered among themselves (one stream, or synchronized); eager calls use
- * other scratch and may interleave.  A graph keeps the store as it was at
- * capture (facts appended later are not searched); once a graph has been
- * captured, is_store_remove refuses (it would free the index the graph
- * reads).
+ * other scratch and may interleave.  A graph searches the facts the store
+ * held at capture (facts appended later are not searched; facts updated
+ * in place are read as updated); once a graph has been captured,
+ * is_store_remove refuses (it would free the index the graph reads).
  * Errors: IS_ERR_INVALID_ARG, IS_ERR_UNSUPPORTED, IS_ERR_DTYPE,
  * IS_ERR_ALIGN, IS_ERR_OOM, IS_ERR_HIP.
  */
