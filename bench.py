@@ -387,48 +387,69 @@ def copy_bandwidth(torch, gib: float = 4.0, reps: int = 5) -> float:
 def cpu_baseline(w, lens, emb, q_bits, flat, req_off, prefix, bt, n_req_sample: int):
     """The fp64 oracle on a bounded sample of the same workload: top-k for
     n_req_sample queries, then inject of those requests into a compact host
-    cache.  Returns (tokens/s, cores, description)."""
+    cache, on all host cores; then the first two requests on one core.
+    Returns (tokens/s, cores, description, single-core tokens/s)."""
     import oracle
+    import synth
     from tests import harness as Hn
 
     cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
-    rows = list(range(n_req_sample))
-    t0 = time.perf_counter()
-    oracle.topk(q_bits[rows], emb, w.k)
-    t_topk = time.perf_counter() - t0
-    sub_off = np.array([req_off[r] for r in rows] + [req_off[rows[-1] + 1]], np.int32)
-    sub_flat = flat[sub_off[0]:sub_off[-1]]
-    sub_bt = bt[rows]
-    blocks = Hn.blocks_of(bt, rows)
-    # inputs for the oracle (generation not timed)
-    uniq = np.unique(sub_flat)
-    row = w.row_elems
-    import synth
-    Kh = np.concatenate([synth.fact_kv(w.seed, synth.TAG_K, int(f), int(lens[f]) * row, w.dtype)
-                         for f in uniq])
-    Vh = np.concatenate([synth.fact_kv(w.seed, synth.TAG_V, int(f), int(lens[f]) * row, w.dtype)
-                         for f in uniq])
-    remap = {int(f): i for i, f in enumerate(uniq)}
-    tok_off = np.zeros(len(uniq) + 1, np.int64)
-    np.cumsum(lens[uniq], out=tok_off[1:])
-    bmap = {int(b): i for i, b in enumerate(blocks)}
-    bt_c = np.vectorize(lambda b: bmap.get(int(b), -1))(sub_bt).astype(np.int32)
-    m = len(blocks)
     B, H, d = w.block_size, w.n_kv_heads, w.head_dim
-    kc = np.zeros(w.n_layers * m * B * H * d, np.uint16)
-    vc = np.zeros_like(kc)
-    strides = (m * B * H * d, B * H * d, H * d, d)
-    ids_c = np.array([remap[int(f)] for f in sub_flat], np.int32)
+    row = w.row_elems
     freqs = Hn.oracle_freqs(w)
-    t0 = time.perf_counter()
-    oracle.inject(w.n_layers, H, d, w.dtype, Kh, Vh, tok_off, sub_off - sub_off[0], ids_c,
-                  prefix[rows], bt_c, B, m, kc, vc, strides, freqs)
-    t_inj = time.perf_counter() - t0
-    tokens = int(lens[sub_flat].sum())
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.topk(q_bits[rows], emb, w.k)
+        t_topk = time.perf_counter() - t0
+        sub_off = np.array([req_off[r] for r in rows] + [req_off[rows[-1] + 1]], np.int32)
+        sub_flat = flat[sub_off[0]:sub_off[-1]]
+        sub_bt = bt[rows]
+        blocks = Hn.blocks_of(bt, rows)
+        # inputs for the oracle (generation not timed)
+        uniq = np.unique(sub_flat)
+        Kh = np.concatenate([synth.fact_kv(w.seed, synth.TAG_K, int(f), int(lens[f]) * row,
+                                           w.dtype) for f in uniq])
+        Vh = np.concatenate([synth.fact_kv(w.seed, synth.TAG_V, int(f), int(lens[f]) * row,
+                                           w.dtype) for f in uniq])
+        remap = {int(f): i for i, f in enumerate(uniq)}
+        tok_off = np.zeros(len(uniq) + 1, np.int64)
+        np.cumsum(lens[uniq], out=tok_off[1:])
+        bmap = {int(b): i for i, b in enumerate(blocks)}
+        bt_c = np.vectorize(lambda b: bmap.get(int(b), -1))(sub_bt).astype(np.int32)
+        m = len(blocks)
+        kc = np.zeros(w.n_layers * m * B * H * d, synth.kv_dtype_np(w.dtype))
+        vc = np.zeros_like(kc)
+        strides = (m * B * H * d, B * H * d, H * d, d)
+        ids_c = np.array([remap[int(f)] for f in sub_flat], np.int32)
+        t0 = time.perf_counter()
+        oracle.inject(w.n_layers, H, d, w.dtype, Kh, Vh, tok_off, sub_off - sub_off[0], ids_c,
+                      prefix[rows], bt_c, B, m, kc, vc, strides, freqs)
+        t_inj = time.perf_counter() - t0
+        return int(lens[sub_flat].sum()), t_topk, t_inj
+
+    tokens, t_topk, t_inj = run(list(range(n_req_sample)))
+    prev = oracle.max_threads()
+    oracle.set_threads(1)
+    try:
+        tok1, t1_topk, t1_inj = run([0, 1][:n_req_sample])
+    finally:
+        oracle.set_threads(prev)
+    one_core = tok1 / (t1_topk + t1_inj)
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     desc = (f"oracle top-{w.k} for {n_req_sample} of {w.n_req} queries ({t_topk:.1f} s) + inject "
             f"of those {n_req_sample} requests, {tokens} tokens ({t_inj:.1f} s); "
-            f"value = tokens / (top-k + inject time)")
-    return tokens / (t_topk + t_inj), cores, desc
+            f"value = tokens / (top-k + inject time); {cores} threads of {model}; one core, "
+            f"the first {min(2, n_req_sample)} requests: {one_core:.0f} tokens/s")
+    return tokens / (t_topk + t_inj), cores, desc, one_core
 
 
 def main() -> int:
@@ -586,10 +607,10 @@ def main() -> int:
     cpu = None
     if args.cpu_sample > 0:
         log(f"CPU oracle baseline on {args.cpu_sample} requests")
-        v, cores, desc = cpu_baseline(w, st.lens, st.emb, q_bits, flat0, req_off, prefix, bt,
-                                      min(args.cpu_sample, n_q))
+        v, cores, desc, one = cpu_baseline(w, st.lens, st.emb, q_bits, flat0, req_off, prefix,
+                                           bt, min(args.cpu_sample, n_q))
         cpu = {"value": round(v, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": desc}
+               "sample": desc, "value_one_core": round(one, 1)}
     st.destroy()
     del cache
     torch.cuda.empty_cache()

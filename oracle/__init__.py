@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
                                 + [c.c_void_p] * 2 + [c.c_int64] * 4 + [c.c_void_p] * 2)
         L.or_attend.restype = c.c_int
         L.or_ingest.argtypes = [c.c_int] * 5 + [c.c_void_p, c.c_int, c.c_void_p, c.c_void_p]
+        L.or_set_threads.argtypes = [c.c_int]
+        L.or_max_threads.restype = c.c_int
         _lib = L
     return _lib
 
@@ -229,3 +231,13 @@ def survivors(n_facts: int, removed) -> np.ndarray:
         raise ValueError("removed ids must be distinct and in range")
     drop = set(gone)
     return np.array([f for f in range(n_facts) if f not in drop], dtype=np.int32)
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only; results do not
+    depend on it)."""
+    lib().or_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().or_max_threads())

@@ -30,6 +30,7 @@
  * dtype; top-k ordered by score descending with ties to the lower id.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -429,3 +430,8 @@ EXPORT void or_ingest(int n_layers, int n_heads, int d, int es, int n, const int
     dst += (int64_t)n_layers * n_heads * len[i] * d * es;
   }
 }
+
+/* Thread count of the parallel loops above (test infrastructure: the bench
+ * times the oracle on all host cores and on one). */
+EXPORT void or_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+EXPORT int or_max_threads(void) { return omp_get_max_threads(); }
