@@ -58,15 +58,17 @@ def _strides(w, nb, layout):
         (nb * B * H * d, H * B * d, d, B * d)
 
 
-@pytest.mark.parametrize("layout,n_qtok,n_q_heads", [
-    ("NHD", 16, 32),   # 64 query rows per kv head: one group of two row tiles
-    ("NHD", 3, 32),    # 12 rows: one tile
-    ("HND", 20, 32),   # 80 rows: two groups on one XCD
-    ("NHD", 5, 8),     # no grouping (g = 1)
+@pytest.mark.parametrize("layout,n_qtok,n_q_heads,block", [
+    ("NHD", 16, 32, 32),   # 64 query rows per kv head: one group of two row tiles
+    ("NHD", 3, 32, 32),    # 12 rows: one tile
+    ("HND", 20, 32, 32),   # 80 rows: two groups on one XCD
+    ("NHD", 5, 8, 32),     # no grouping (g = 1)
+    ("NHD", 16, 32, 8),    # 8-slot blocks: a 32-token chunk spans 4-5 table entries
 ])
-def test_attend_matches_oracle_on_the_same_cache(gpu, layout, n_qtok, n_q_heads):
+def test_attend_matches_oracle_on_the_same_cache(gpu, layout, n_qtok, n_q_heads, block):
     import torch
-    w = W.WORKLOADS["mistral7b_batch"].scaled(name="attend", n_layers=2, n_blocks=64)
+    w = W.WORKLOADS["mistral7b_batch"].scaled(name="attend", n_layers=2, block_size=block,
+                                              n_blocks=64 * 32 // block)
     nb, B, H, d, L = w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim, w.n_layers
     n = L * nb * B * H * d
     kc = synth.fact_kv(w.seed, synth.TAG_K, 1_000_000, n, synth.BF16)
@@ -87,7 +89,8 @@ def test_attend_matches_oracle_on_the_same_cache(gpu, layout, n_qtok, n_q_heads)
         bt[r, :need[r]] = perm[(r * 7) % 10:(r * 7) % 10 + need[r]]
     q = synth.fact_kv(w.seed, synth.TAG_K, 2_000_000, L * n_req * n_qtok * n_q_heads * d,
                       synth.BF16).reshape(L, n_req, n_qtok, n_q_heads, d)
-    Hn.log(f"attend: {layout}, {n_qtok} tokens x {n_q_heads} heads, contexts {list(ce - cb)}")
+    Hn.log(f"attend: {layout}, {n_qtok} tokens x {n_q_heads} heads, block {block}, "
+           f"contexts {list(ce - cb)}")
     st = _store_only(w)
     try:
         got = _gpu_attend(st, w, cache, q, q_pos, cb, ce, bt, n_q_heads)
