@@ -1016,19 +1016,24 @@ IS_EXPORT int is_store_remove(is_store* s, int64_t n, const int32_t* ids, void* 
   std::memcpy(h + o_keep, keep.data(), (size_t)m * 4);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
+  // the new index arena first: an allocation failure must leave the store as it was
   uint16_t* emb = nullptr;
+  if (s->emb_dim > 0 && hipMalloc((void**)&emb, s->emb_alloc_bytes()) != hipSuccess)
+    return fail(IS_ERR_OOM, "embedding arena");
   if (m > 0) {
     if ((e = hipMemcpyAsync(dv, h, tab_bytes, hipMemcpyHostToDevice, st)) != hipSuccess ||
         (e = hipMemcpyAsync(s->d_len, dv, (size_t)m * 4, hipMemcpyDeviceToDevice, st)) != hipSuccess ||
         (e = hipMemcpyAsync(s->d_k_addr, dv + o_k, (size_t)m * 8, hipMemcpyDeviceToDevice, st)) !=
             hipSuccess ||
         (e = hipMemcpyAsync(s->d_v_addr, dv + o_v, (size_t)m * 8, hipMemcpyDeviceToDevice, st)) !=
-            hipSuccess)
+            hipSuccess) {
+      (void)hipStreamSynchronize(st);
+      if (emb) (void)hipFree(emb);
       return hip_fail(e, "fact table update");
+    }
   }
   if (s->emb_dim > 0) {
     const size_t bytes = s->emb_alloc_bytes();
-    if (hipMalloc((void**)&emb, bytes) != hipSuccess) return fail(IS_ERR_OOM, "embedding arena");
     if ((e = hipMemsetAsync(emb, 0, bytes, st)) != hipSuccess ||
         (e = is::launch_emb_compact(s->emb, reinterpret_cast<const int32_t*>(dv + o_keep), m,
                                     s->emb_dim, emb, st)) != hipSuccess) {
