@@ -328,22 +328,24 @@ int is_store_remove(is_store* s, int64_t n, const int32_t* ids, void* stream);
  *               * V_l[slot_r(p)][hq / g],  p in [ctx_begin[r], ctx_end[r])
  * with slot_r(p) = block_tables[r][p / block_size] * block_size
  * + p % block_size; an empty context gives zeros.
- *   q     device [n_layers][n_req][n_qtok][n_q_heads][head_dim] bf16 bits,
- *         before RoPE (rotated here in fp32), 16-byte aligned
+ *   q     device [n_layers][n_req][n_qtok][n_q_heads][head_dim] in the store's
+ *         dtype (bf16 bits or fp32), before RoPE (rotated here in fp32),
+ *         16-byte aligned
  *   out   device fp32, same shape, 16-byte aligned
  *   q_pos, ctx_begin, ctx_end   host [n_req]
  *   block_tables                host [n_req][max_blocks]
- * Products run on the matrix cores with the fp32 operands (rotated query,
- * probabilities) split into two bf16 parts; accumulation is fp32.
+ * bf16 stores with head_dim 128 run on the matrix cores, the fp32 operands
+ * (rotated query, probabilities) split into two bf16 parts, accumulation in
+ * fp32; other head dims (even, at most 256) and fp32 stores run a plain
+ * fp32 kernel (one wave per query row), a parity path for small shapes.
  * Validation before any work: positions in [0, 2^24), 0 <= begin <= end,
  * block tables cover every context position with entries in [0, n_blocks).
  * Host arrays are copied before return; the kernel runs on `stream`.
- * Covers bf16 stores with head_dim 128 (else IS_ERR_UNSUPPORTED).
  * Errors: IS_ERR_INVALID_ARG, IS_ERR_BLOCK_TABLE, IS_ERR_DTYPE, IS_ERR_ALIGN,
- * IS_ERR_UNSUPPORTED, IS_ERR_OOM, IS_ERR_HIP.
+ * IS_ERR_UNSUPPORTED (head_dim above 256), IS_ERR_OOM, IS_ERR_HIP.
  */
 int is_attend(const is_store* s, const is_cache* cache, const is_rope* rope, int32_t n_req,
-              int32_t n_qtok, int32_t n_q_heads, const uint16_t* q, const int32_t* q_pos,
+              int32_t n_qtok, int32_t n_q_heads, const void* q, const int32_t* q_pos,
               const int32_t* ctx_begin, const int32_t* ctx_end, const int32_t* block_tables,
               int32_t max_blocks, float* out, void* stream);
 

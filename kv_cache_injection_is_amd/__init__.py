@@ -199,8 +199,9 @@ def is_retrieve_inject(store: int, q_f16, n_req: int, k: int, prefix_len, block_
 def is_attend(store: int, cache: is_cache, rope: is_rope, q, n_qtok: int, n_q_heads: int,
               q_pos, ctx_begin, ctx_end, block_tables, out, stream=None) -> None:
     """q, out: device tensors [n_layers][n_req][n_qtok][n_q_heads][head_dim]
-    (bf16 bits as int16/uint16, float32); q_pos, ctx_begin, ctx_end ([n_req])
-    and block_tables ([n_req][max_blocks]) are host arrays."""
+    (q in the store's dtype: bf16 bits as int16/uint16, or float32; out
+    float32); q_pos, ctx_begin, ctx_end ([n_req]) and block_tables
+    ([n_req][max_blocks]) are host arrays."""
     qp, qp_p = _host(q_pos, np.int32)
     cb, cb_p = _host(ctx_begin, np.int32)
     ce, ce_p = _host(ctx_end, np.int32)

@@ -712,15 +712,14 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
 }
 
 IS_EXPORT int is_attend(const is_store* cs, const is_cache* cache, const is_rope* rope,
-                        int32_t n_req, int32_t n_qtok, int32_t n_q_heads, const uint16_t* q,
+                        int32_t n_req, int32_t n_qtok, int32_t n_q_heads, const void* q,
                         const int32_t* q_pos, const int32_t* ctx_begin, const int32_t* ctx_end,
                         const int32_t* block_tables, int32_t max_blocks, float* out,
                         void* stream) {
   is::clear_error();
   if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
   is_store* s = const_cast<is_store*>(cs);
-  if (s->dtype != IS_DTYPE_BF16 || s->d != 128)
-    return fail(IS_ERR_UNSUPPORTED, "attention covers bf16 caches with head_dim 128");
+  if (s->d > 256) return fail(IS_ERR_UNSUPPORTED, "attention covers head_dim up to 256");
   int rc = is::check_cache(s->dtype, cache);
   if (rc != IS_OK) return rc;
   rc = is::check_rope(rope);
@@ -796,6 +795,8 @@ IS_EXPORT int is_attend(const is_store* cs, const is_cache* cache, const is_rope
   a.n_qtok = n_qtok;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = s->H;
+  a.head_dim = s->d;
+  a.dtype = s->dtype;
   a.max_blocks = max_blocks;
   a.block_size = cache->block_size;
   a.rows = n_qtok * (n_q_heads / s->H);

@@ -241,7 +241,8 @@ __global__ __launch_bounds__(QT * NS * 64) void attend_kernel(AttendLaunch a) {
     float x[2][8];
     if (R < a.rows) {
       const int t = R / G, hq = kvh * G + R % G;
-      const uint16_t* qp = a.q + ((((int64_t)layer * a.n_req + r) * a.n_qtok + t) *
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                           ((((int64_t)layer * a.n_req + r) * a.n_qtok + t) *
                                   a.n_q_heads + hq) * kD;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -423,10 +424,102 @@ __global__ __launch_bounds__(QT * NS * 64) void attend_kernel(AttendLaunch a) {
   }
 }
 
+// Any head_dim (even, at most 256) and cache dtype (fp32 or bf16), for the
+// shapes the matrix-core kernel does not take: one wave per query row
+// (layer, request, query token, query head).  Lane j holds the rotation
+// pairs (j, j + d/2) and (j + 64, j + 64 + d/2) of the query and of every
+// key and value row it reads; a score is a wave-wide sum; the online softmax
+// (base 2) and the output accumulate in fp32.  Plain loads, one context
+// token after the other: a parity path for small shapes, not a fast one.
+template <typename T>
+__device__ __forceinline__ float elem(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float elem<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_value(p[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void attend_generic(AttendLaunch a) {
+  const int64_t row = blockIdx.x;
+  const int hq = (int)(row % a.n_q_heads);
+  const int t = (int)((row / a.n_q_heads) % a.n_qtok);
+  const int r = (int)((row / ((int64_t)a.n_q_heads * a.n_qtok)) % a.n_req);
+  const int layer = (int)(row / ((int64_t)a.n_q_heads * a.n_qtok * a.n_req));
+  const int kvh = hq / (a.n_q_heads / a.n_kv_heads);
+  const int lane = threadIdx.x;
+  const int half = a.head_dim / 2;
+  const int qpos = a.meta[3 * r] + t, cb = a.meta[3 * r + 1], ce = a.meta[3 * r + 2];
+  const float scale = 1.4426950408889634f / sqrtf((float)a.head_dim);   // log2(e) / sqrt(d)
+  const T* q = static_cast<const T*>(a.q) + row * a.head_dim;
+  float qa[2], qb[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = lane + 64 * u;
+    qa[u] = qb[u] = 0.f;
+    if (i < half) {
+      const float x = elem<T>(q, i), y = elem<T>(q, i + half);
+      const float2 cs = sincos_of_turns(qpos, a.g[i].x, a.g[i].y);
+      qa[u] = __builtin_fmaf(x, cs.x, -(y * cs.y)) * scale;
+      qb[u] = __builtin_fmaf(y, cs.x, x * cs.y) * scale;
+    }
+  }
+  const T* kc = static_cast<const T*>(a.kc);
+  const T* vc = static_cast<const T*>(a.vc);
+  const int32_t* bt = a.bt + (int64_t)r * a.max_blocks;
+  const int64_t head_off = (int64_t)layer * a.s_layer + (int64_t)kvh * a.s_head;
+  float m = -1e30f, l = 0.f, oa[2] = {0.f, 0.f}, ob[2] = {0.f, 0.f};
+  for (int p = cb; p < ce; ++p) {
+    const int64_t off = head_off + (int64_t)bt[p / a.block_size] * a.s_block +
+                        (int64_t)(p % a.block_size) * a.s_slot;
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = lane + 64 * u;
+      if (i < half)
+        part += qa[u] * elem<T>(kc, off + i) + qb[u] * elem<T>(kc, off + i + half);
+    }
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) part += __shfl_xor(part, w);
+    const float mn = fmaxf(m, part);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn), wgt = __builtin_amdgcn_exp2f(part - mn);
+    m = mn;
+    l = l * alpha + wgt;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = lane + 64 * u;
+      if (i < half) {
+        oa[u] = oa[u] * alpha + wgt * elem<T>(vc, off + i);
+        ob[u] = ob[u] * alpha + wgt * elem<T>(vc, off + i + half);
+      }
+    }
+  }
+  float* out = a.out + row * a.head_dim;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = lane + 64 * u;
+    if (i < half) {
+      out[i] = l > 0.f ? oa[u] / l : 0.f;
+      out[i + half] = l > 0.f ? ob[u] / l : 0.f;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attend(const AttendLaunch& in, hipStream_t stream) {
   if (in.n_units == 0 || in.rows == 0) return hipSuccess;
+  if (in.dtype != IS_DTYPE_BF16 || in.head_dim != kD) {
+    if (in.head_dim < 2 || in.head_dim % 2 != 0 || in.head_dim > 256) return hipErrorInvalidValue;
+    const int64_t rows = (int64_t)in.n_layers * in.n_req * in.n_qtok * in.n_q_heads;
+    if (rows > INT32_MAX) return hipErrorInvalidValue;
+    if (in.dtype == IS_DTYPE_F32)
+      hipLaunchKernelGGL(attend_generic<float>, dim3((unsigned)rows), dim3(64), 0, stream, in);
+    else
+      hipLaunchKernelGGL(attend_generic<uint16_t>, dim3((unsigned)rows), dim3(64), 0, stream, in);
+    return hipGetLastError();
+  }
   AttendLaunch a = in;
   const int qt = a.rows <= 32 ? 1 : 2;
   a.groups = (a.rows + qt * 32 - 1) / (qt * 32);

@@ -63,7 +63,7 @@ struct AttendLaunch {
   const void* kc;           // cache bases
   const void* vc;
   int64_t s_layer, s_block, s_slot, s_head;   // cache strides (elements)
-  const uint16_t* q;        // [n_layers][n_req][n_qtok][n_q_heads][128] bf16, before RoPE
+  const void* q;            // [n_layers][n_req][n_qtok][n_q_heads][head_dim], cache dtype, before RoPE
   float* out;               // same shape, fp32
   const int32_t* meta;      // [n_req][3]: position of query token 0, context begin, end
   const int32_t* bt;        // [n_req][max_blocks]
@@ -72,6 +72,8 @@ struct AttendLaunch {
   int32_t n_layers, n_req, n_qtok, n_q_heads, n_kv_heads, max_blocks, block_size;
   int32_t rows;             // n_qtok * (n_q_heads / n_kv_heads)
   int32_t groups;           // derived by launch_attend
+  int32_t head_dim;         // 128 on the matrix-core path; any even value <= 256 otherwise
+  int32_t dtype;            // IS_DTYPE_BF16 or IS_DTYPE_F32 (cache, and q)
 };
 
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t stream);

@@ -155,3 +155,95 @@ def test_attend_rejects_bad_tables_without_gpu_work(gpu):
             assert e.value.code == code
     finally:
         Hn.K.is_store_destroy(st)
+
+
+def _dev_q(q):
+    import torch
+    return torch.from_numpy(q if q.dtype == np.float32 else q.view(np.int16)).cuda()
+
+
+@pytest.mark.parametrize("dtype,d,H,G", [
+    (synth.F32, 64, 2, 2),     # the tiny configuration's cache type and head size
+    (synth.BF16, 64, 4, 4),
+    (synth.BF16, 256, 2, 1),
+])
+def test_attend_plain_kernel_matches_oracle(gpu, dtype, d, H, G):
+    """Shapes off the matrix-core path (fp32 caches, head_dim other than 128)
+    run the plain fp32 kernel; same caches on both sides."""
+    import torch
+    w = W.WORKLOADS["tiny"].scaled(name="attend_plain", n_layers=2, n_kv_heads=H, head_dim=d,
+                                   dtype=dtype, block_size=16, n_blocks=64)
+    nb, B, L = w.n_blocks, w.block_size, w.n_layers
+    n = L * nb * B * H * d
+    kc = synth.fact_kv(w.seed, synth.TAG_K, 3_000_000, n, dtype)
+    vc = synth.fact_kv(w.seed, synth.TAG_V, 3_000_000, n, dtype)
+    cache = Hn.make_cache(w)
+    cache.k.copy_(torch.from_numpy(kc.view(np.uint8)))
+    cache.v.copy_(torch.from_numpy(vc.view(np.uint8)))
+    n_req, n_qtok, n_q_heads = 4, 3, H * G
+    cb = np.array([3, 0, 10, 2], np.int32)
+    ce = np.array([70, 17, 10, 300], np.int32)
+    q_pos = ce + np.array([0, 4, 1, 9], np.int32)
+    need = (ce + B - 1) // B
+    bt = np.full((n_req, int(need.max())), -1, np.int32)
+    perm = synth.permutation(w.seed, nb)
+    for r in range(n_req):
+        bt[r, :need[r]] = perm[r:r + need[r]]
+    q = synth.fact_kv(w.seed, synth.TAG_K, 4_000_000, L * n_req * n_qtok * n_q_heads * d,
+                      dtype).reshape(L, n_req, n_qtok, n_q_heads, d)
+    Hn.log(f"attend (plain kernel): dtype {dtype}, head_dim {d}, {H} kv heads x {G}")
+    st = _store_only(w)
+    try:
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        Hn.K.is_attend(st, cache.desc, Hn.rope_of(w), _dev_q(q), n_qtok, n_q_heads, q_pos, cb,
+                       ce, bt, out, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+    finally:
+        Hn.K.is_store_destroy(st)
+    ref = oracle.attend(L, H, n_q_heads, d, dtype, q, q_pos, cb, ce, bt, B, nb, kc, vc,
+                        _strides(w, nb, "NHD"), Hn.oracle_freqs(w))
+    err = np.abs(got - ref)
+    Hn.log(f"  max |gpu - oracle| = {err.max():.3g}")
+    assert err.max() <= SAME_CACHE_TOL
+    assert np.array_equal(got[:, 2], np.zeros_like(got[:, 2]))    # empty context
+
+
+def test_attend_after_inject_tiny_theorem6(gpu):
+    """The tiny fp32 configuration end to end: facts injected on the GPU,
+    then attended from query tokens right after the segment, against the
+    oracle's keys prefilled at the same positions (fp32 caches: the inject
+    tolerance is 1e-5 per element)."""
+    import torch
+    w = W.WORKLOADS["tiny"].scaled(name="attend_tiny", n_blocks=64)
+    lens = W.fact_lengths(w)
+    ids = np.array([[3, 11, 7, 0, 19]], np.int32)
+    req_off, flat = Hn.requests_from_ids(ids)
+    prefix = np.array([16], np.int32)
+    T = int(lens[flat].sum())
+    bt = Hn.block_tables_for(w, lens, req_off, flat, prefix)
+    st = Hn.make_store(w, lens)
+    try:
+        cache = Hn.make_cache(w)
+        Hn.gpu_inject(st, cache, req_off, flat, prefix, bt)
+        n_qtok, n_q_heads = 4, 2 * w.n_kv_heads
+        q = synth.fact_kv(w.seed, synth.TAG_V, 5_000_000,
+                          w.n_layers * 1 * n_qtok * n_q_heads * w.head_dim,
+                          synth.F32).reshape(w.n_layers, 1, n_qtok, n_q_heads, w.head_dim)
+        cb, ce = prefix.astype(np.int32), (prefix + T).astype(np.int32)
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        Hn.K.is_attend(st.handle, cache.desc, Hn.rope_of(w), _dev_q(q), n_qtok, n_q_heads, ce,
+                       cb, ce, bt, out, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+    finally:
+        st.destroy()
+    kc_o, vc_o = Hn.oracle_blocks(w, lens, req_off, flat, prefix, bt, np.arange(w.n_blocks),
+                                  "NHD", w.n_blocks)
+    ref = oracle.attend(w.n_layers, w.n_kv_heads, n_q_heads, w.head_dim, synth.F32, q, ce, cb,
+                        ce, bt, w.block_size, w.n_blocks, kc_o.view(np.float32),
+                        vc_o.view(np.float32), _strides(w, w.n_blocks, "NHD"),
+                        Hn.oracle_freqs(w))
+    err = np.abs(got - ref)
+    Hn.log(f"  max |gpu inject+attend - oracle prefill+attend| (tiny) = {err.max():.3g}")
+    assert err.max() <= 5e-4
