@@ -113,7 +113,10 @@ struct TopkLaunch {
   int32_t n_q;
   int32_t k;
   int32_t scan_wgs;       // derived by launch_topk
-  // derived by launch_topk
+  // derived by launch_topk; n_tiles and sample_tiles count scan tiles of
+  // scan_tile facts (the scan kernel's tile: 256, or 128 for the variant
+  // that keeps the queries in registers)
+  int32_t scan_tile;
   int64_t n_tiles, sample_n, sample_tiles, n_groups, cand_stride;
   // scratch (see topk_scratch)
   uint16_t* q_pad;        // [n_q][padded_dim] when emb_dim % 64 != 0

@@ -38,6 +38,10 @@
 
 #include "kernels.h"
 
+#ifndef IS_TOPK_RESIDENT
+#define IS_TOPK_RESIDENT 1   // full batches at width 1024 keep their queries in registers
+#endif
+
 namespace is {
 namespace {
 
@@ -111,6 +115,16 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t a) {
 }
 
 typedef __attribute__((address_space(3))) char* lds_cptr;
+
+// Scores of a lane's MFMA fragment whose facts lie past the store: element
+// e is fact f0 + 8 * (e / 4) + e % 4, and `room` = n_facts - f0.  Only the
+// tile holding the store's last fact calls it, so the other tiles' epilogue
+// is a 16-way maximum and a compare.
+__device__ __forceinline__ void mask_padding(float (&v)[16], int32_t room) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (8 * (e / 4) + (e % 4) >= room) v[e] = -INFINITY;
+}
 
 struct ScanSmem {
   u32x4 e[kStages][kEPieces];
@@ -244,7 +258,6 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
 
   float16v acc[2][QT];
   auto emit = [&](int64_t t) {
-    const bool edge = (t == edge_tile);
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft) {
       // element e of a lane's fragment is fact f0 + 8 * (e / 4) + e % 4
@@ -254,10 +267,8 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
         const int q = qt * 32 + row;
         float v[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          v[e] = acc[ft][qt][e];
-          if (edge && f0 + 8 * (e / 4) + (e % 4) >= a.n_facts) v[e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e) v[e] = acc[ft][qt][e];
+        if (t == edge_tile) mask_padding(v, (int32_t)(a.n_facts - f0));   // uniform branch
         float mx = v[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
@@ -319,6 +330,238 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
   if (!kSample) {
     __syncthreads();
     if (tid < a.n_q) a.count[(int64_t)tid * kTopkMaxScanWG + w] = sm.count[tid];
+  }
+}
+
+// Scan variant for full query batches (65..128 queries) at width 1024.
+// The query rows are the same for every tile, so instead of re-staging them
+// through LDS for every chunk, each wave keeps its own 32 query rows -- all
+// 1024 dims, 256 registers per lane -- for the whole launch, and the LDS
+// ring holds fact rows only: eight stages of a 128-fact x 64-dim block
+// (16 KB, one half of a stored 256 x 64 block), seven of them in flight
+// while one is scored.  Every wave scores all 128 facts of a stage against
+// its 32 queries (four v_mfma_f32_32x32x16_f16 row tiles per k-step), so all
+// waves read every stage and one barrier per chunk both publishes a stage
+// and frees the one scored before it.  With 16 chunks per tile and 8 stages
+// the ring slot of a chunk is fixed by its index in the tile, which keeps
+// the query registers and the ring addressing static.
+constexpr int kRFT = 128;                       // facts per tile
+constexpr int kRChunks = 16;                    // 64-dim chunks of a 1024-wide row
+constexpr int kRStages = 8;
+constexpr int kRPieces = kRFT * kKC / 8;        // 16-byte pieces of a stage
+constexpr int kRDma = kRPieces / 64 / kWaves;   // transfers per wave per stage
+static_assert(kRChunks % kRStages == 0, "ring slot must be static per chunk");
+constexpr int64_t kResidentMinFacts = (int64_t)4 * kTopkMaxScanWG * kRFT;   // 131,072
+static_assert(kQB == kWaves * 32, "one 32-query tile per wave");
+
+// Candidates found during the stream are staged in LDS and written out
+// after the loop: a global store counts in vmcnt like the ring's transfers,
+// and, issued behind seven chunks in flight, it would make every ring wait
+// of the next steps wait for that much more.  Each wave owns its queries,
+// so it also owns their candidates: a query's running count lives in the
+// registers of its two lanes, and each wave fills its own part of the
+// staging area, slots taken by a ballot prefix sum (no atomics).  An
+// entry's destination is (query << 25) | position in the query's region;
+// a wave whose part is full stores further candidates directly.
+constexpr int kCandWave = 512;   // staged candidates per wave
+constexpr int kPosBits = 25;
+
+struct ScanSmemQR {
+  u32x4 e[kRStages][kRPieces];
+  uint64_t ckey[kWaves][kCandWave];
+  uint32_t cdst[kWaves][kCandWave];
+};
+
+// Exclusive prefix sum over the wave of n (0 <= n <= 64) and the wave's
+// total, bit by bit from ballots.
+__device__ __forceinline__ uint32_t wave_prefix(uint32_t n, uint32_t& total) {
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 7; ++b) {
+    const uint64_t bal = __ballot((n >> b) & 1u);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    pre += below << b;
+    tot += (uint32_t)__builtin_popcountll(bal) << b;
+  }
+  total = tot;
+  return pre;
+}
+
+// Waits until at most 4 * n of this wave's ring transfers are in flight.
+__device__ __forceinline__ void wait_chunks(int n) {
+  static_assert(kRDma == 4, "wait counts assume four transfers per stage");
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<4>(); break;
+    case 2: wait_vm<8>(); break;
+    case 3: wait_vm<12>(); break;
+    case 4: wait_vm<16>(); break;
+    case 5: wait_vm<20>(); break;
+    default: wait_vm<24>(); break;
+  }
+}
+
+template <bool kSample>
+__global__ __launch_bounds__(kThreads) void topk_scan_qr(TopkLaunch a) {
+  __shared__ ScanSmemQR sm;
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int row = lane % 32;
+  const int grp = lane / 32;
+  const int G = (int)gridDim.x;
+  const int w = (int)blockIdx.x;
+  const int64_t n_tiles = kSample ? a.sample_tiles : a.n_tiles;
+  const int my_tiles = (int)((n_tiles - w + G - 1) / G);
+  const int total = my_tiles * kRChunks;
+  const int64_t edge_tile = (a.n_facts - 1) / kRFT;
+  const int q = wave * 32 + row;   // this lane's query (column of every score tile)
+  const bool q_ok = q < a.n_q;
+  const float tau = (!kSample && q_ok) ? a.tau[q] : 0.f;
+  const uint64_t region0 = (uint64_t)region_tile(w, n_tiles, G) * kRFT;
+  const bool stage_ok = (int64_t)my_tiles * kRFT <= ((int64_t)1 << kPosBits);
+  uint32_t q_count = 0;    // candidates of this lane's query so far (both its lanes)
+  uint32_t staged = 0;     // this wave's staging slots used (wave-uniform)
+
+  // k-step s of chunk c multiplies dims c*64 + (2s + grp)*8 .. +8 of both
+  // operands (the dot product is order-free in k); rows past n_q take row 0
+  // and their scores are never used.
+  half8 qv[kRChunks * 4];
+  {
+    const uint16_t* src = a.q + (int64_t)(q_ok ? q : 0) * (kRChunks * kKC) + grp * 8;
+#pragma unroll
+    for (int j = 0; j < kRChunks * 4; ++j)
+      qv[j] = *reinterpret_cast<const half8*>(src + j * 16);
+  }
+
+  const uint32_t e_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.e[0][0];
+  // Issue cursor: tile et (in 128-fact tiles), chunk ec.  Tile et is half
+  // et & 1 of stored 256-fact tile et >> 1, whose chunk ec is one 32 KB span.
+  int64_t et = w;
+  int ec = 0;
+  auto issue = [&](int slot_stage) {
+    const uint16_t* blk =
+        a.emb + (((et >> 1) * kRChunks + ec) * kFT + (et & 1) * kRFT) * (int64_t)kKC;
+#pragma unroll
+    for (int i = 0; i < kRDma; ++i) {
+      const int s0 = (wave * kRDma + i) * 64;
+      const int slot = s0 + lane;
+      const int r = slot >> 3, p = (slot & 7) ^ ((r >> 1) & 7);
+      dma16(blk + r * kKC + p * 8,
+            __builtin_amdgcn_readfirstlane(e_lds + (uint32_t)((slot_stage * kRPieces + s0) * 16)));
+    }
+    if (++ec == kRChunks) {
+      ec = 0;
+      et += G;
+    }
+  };
+
+  float16v acc[kRFT / 32];
+  auto emit = [&](int64_t t) {
+    float v[kRFT / 32][16];
+    uint32_t m[kRFT / 32];
+    uint32_t n = 0;
+#pragma unroll
+    for (int ft = 0; ft < kRFT / 32; ++ft) {
+      // element e of a lane's fragment is fact f0 + 8 * (e / 4) + e % 4
+      const int64_t f0 = t * kRFT + ft * 32 + 4 * grp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[ft][e] = acc[ft][e];
+      if (t == edge_tile) mask_padding(v[ft], (int32_t)(a.n_facts - f0));   // uniform branch
+      float mx = v[ft][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[ft][e]);
+      if (kSample) {
+        if (q_ok) {
+          const int64_t gi = (t * (kRFT / 32) + ft) * 2 + grp;
+          a.gmax[(int64_t)q * a.n_groups + gi] = (mx == -INFINITY) ? 0u : ord_of(mx);
+        }
+      } else {
+        m[ft] = 0;
+        if (q_ok && mx >= tau) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m[ft] |= (v[ft][e] >= tau) ? (1u << e) : 0u;
+        }
+        n += (uint32_t)__builtin_popcount(m[ft]);
+      }
+    }
+    if (kSample || !__any(n != 0)) return;
+    // positions in the query's region: the grp 0 lane's candidates first
+    const uint32_t n_pair = __shfl_xor(n, 32);
+    uint32_t pos = q_count + (grp ? n_pair : 0u);
+    q_count += n + n_pair;
+    uint32_t wave_n;
+    uint32_t slot = staged + wave_prefix(n, wave_n);
+    staged += wave_n;
+    uint64_t* direct = a.cand + (int64_t)q * a.cand_stride + region0;
+#pragma unroll
+    for (int ft = 0; ft < kRFT / 32; ++ft) {
+      const uint32_t f0 = (uint32_t)(t * kRFT + ft * 32 + 4 * grp);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (m[ft] & (1u << e)) {
+          const uint64_t key = key_of(ord_of(v[ft][e]), f0 + 8 * (e / 4) + (e % 4));
+          if (stage_ok && slot < (uint32_t)kCandWave) {
+            sm.ckey[wave][slot] = key;
+            sm.cdst[wave][slot] = ((uint32_t)q << kPosBits) | pos;
+          } else {
+            direct[pos] = key;
+          }
+          ++slot;
+          ++pos;
+        }
+    }
+  };
+
+  // One chunk: `after` = chunks of this workgroup still to come after it
+  // (a constant once the chunk loop is unrolled; kRChunks for every tile
+  // but the last).  All 16 fragments of the stage are read before the 16
+  // MFMAs, so the chunk pays one LDS latency rather than one per MFMA.
+  auto step = [&](int c, int after) {
+    wait_chunks(after < kRStages - 2 ? after : kRStages - 2);
+    ring_barrier();   // chunk c landed for every wave; the previous stage is free
+    if (after >= kRStages - 1) issue((c + kRStages - 1) % kRStages);
+    const u32x4* es = sm.e[c % kRStages];
+    half8 av[kKC / 16][kRFT / 32];
+#pragma unroll
+    for (int s = 0; s < kKC / 16; ++s)
+#pragma unroll
+      for (int ft = 0; ft < kRFT / 32; ++ft)
+        av[s][ft] = __builtin_bit_cast(half8, es[piece_slot(ft * 32 + row, 2 * s + grp)]);
+    __builtin_amdgcn_sched_barrier(0);
+    const float16v zero = {};
+#pragma unroll
+    for (int s = 0; s < kKC / 16; ++s)
+#pragma unroll
+      for (int ft = 0; ft < kRFT / 32; ++ft)
+        acc[ft] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            av[s][ft], qv[c * 4 + s], (c == 0 && s == 0) ? zero : acc[ft], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // total >= 16 > kRStages - 1: the prologue always fills the ring.
+#pragma unroll
+  for (int g = 0; g < kRStages - 1; ++g) issue(g);
+  int64_t ct = w;
+  for (int i = 0; i + 1 < my_tiles; ++i) {
+#pragma unroll
+    for (int c = 0; c < kRChunks; ++c) step(c, kRChunks);
+    emit(ct);
+    ct += G;
+  }
+#pragma unroll
+  for (int c = 0; c < kRChunks; ++c) step(c, kRChunks - 1 - c);
+  emit(ct);
+  wait_vm<0>();
+  if (!kSample) {
+    if (grp == 0 && q_ok) a.count[(int64_t)q * kTopkMaxScanWG + w] = q_count;
+    // the wave's own staged entries (written by this wave only)
+    const uint32_t used = !stage_ok ? 0u : staged < (uint32_t)kCandWave ? staged : (uint32_t)kCandWave;
+    for (uint32_t i = lane; i < used; i += 64) {
+      const uint32_t d = sm.cdst[wave][i];
+      a.cand[(int64_t)(d >> kPosBits) * a.cand_stride + region0 + (d & ((1u << kPosBits) - 1))] =
+          sm.ckey[wave][i];
+    }
   }
 }
 
@@ -437,7 +680,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
     total += wtot[w2];
   }
   const uint64_t* mine =
-      a.cand + (int64_t)q * a.cand_stride + (tid < G ? region_tile(tid, a.n_tiles, G) * kFT : 0);
+      a.cand + (int64_t)q * a.cand_stride +
+      (tid < G ? region_tile(tid, a.n_tiles, G) * a.scan_tile : 0);
   auto take = [&](uint64_t v, uint64_t thr) {
     if (v >= thr) {
       const uint32_t slot = atomicAdd(&n_best, 1u);   // at most k keys pass
@@ -568,13 +812,22 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
       in.emb_dim % 8 != 0)
     return hipErrorInvalidValue;
   TopkLaunch a = in;
-  a.n_tiles = (a.n_facts + kFT - 1) / kFT;
-  a.sample_n = topk_sample_size(a.n_facts);
-  a.sample_tiles = (a.sample_n + kFT - 1) / kFT;
-  a.n_groups = a.sample_tiles * kTopkGroupsPerTile;
-  a.cand_stride = a.n_tiles * kFT;
-  a.scan_wgs = (int32_t)(a.n_tiles < kTopkMaxScanWG ? a.n_tiles : kTopkMaxScanWG);
   const int32_t padded = topk_padded_dim(a.emb_dim);
+  // query tiles of 32 the launch fills: 1, 2 or 4.  Full batches at width
+  // 1024 over large stores keep their queries in registers (128-fact tiles);
+  // below kResidentMinFacts (4 tiles per workgroup) a workgroup's chunks are
+  // too few to fill the deeper ring, and the staged scan's 32 KB steps are
+  // fewer.  Sample and stream scan always use the same kernel.
+  const int qt = a.n_q <= 32 ? 1 : a.n_q <= 64 ? 2 : 4;
+  const bool resident = IS_TOPK_RESIDENT && qt == 4 && padded == kRChunks * kKC &&
+                        a.n_facts >= kResidentMinFacts;
+  a.scan_tile = resident ? kRFT : kFT;
+  a.n_tiles = (a.n_facts + a.scan_tile - 1) / a.scan_tile;
+  a.sample_n = topk_sample_size(a.n_facts);
+  a.sample_tiles = (a.sample_n + a.scan_tile - 1) / a.scan_tile;
+  a.n_groups = a.sample_tiles * (a.scan_tile / 16);   // groups of 16 facts
+  a.cand_stride = topk_padded_facts(a.n_facts);
+  a.scan_wgs = (int32_t)(a.n_tiles < kTopkMaxScanWG ? a.n_tiles : kTopkMaxScanWG);
   if (padded != a.emb_dim) {
     const int64_t n = (int64_t)a.n_q * padded;
     hipLaunchKernelGGL(pad_queries, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
@@ -583,11 +836,12 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
     a.emb_dim = padded;
   }
   const int sample_wgs = (int)(a.sample_tiles < kTopkMaxScanWG ? a.sample_tiles : kTopkMaxScanWG);
-  // query tiles of 32 the launch fills: 1, 2 or 4
-  const int qt = a.n_q <= 32 ? 1 : a.n_q <= 64 ? 2 : 4;
   auto scan = [&](bool sample, unsigned wgs) {
     const dim3 g(wgs), b(kThreads);
-    if (sample) {
+    if (resident) {
+      if (sample) hipLaunchKernelGGL(topk_scan_qr<true>, g, b, 0, stream, a);
+      else hipLaunchKernelGGL(topk_scan_qr<false>, g, b, 0, stream, a);
+    } else if (sample) {
       if (qt == 1) hipLaunchKernelGGL((topk_scan<true, 1>), g, b, 0, stream, a);
       else if (qt == 2) hipLaunchKernelGGL((topk_scan<true, 2>), g, b, 0, stream, a);
       else hipLaunchKernelGGL((topk_scan<true, 4>), g, b, 0, stream, a);

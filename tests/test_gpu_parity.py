@@ -169,6 +169,10 @@ def test_inject_invalid_call_writes_nothing(gpu):
     (3000, 256, 130, 64),    # two query blocks, k at its maximum
     (2000, 192, 40, 20),     # two 32-query tiles, width not a multiple of 128
     (70000, 128, 3, 1),      # all 256 workgroups, several tiles each
+    (140001, 1024, 100, 50), # queries held in registers (stores of 131,072 facts and
+                             # more): 1,094 tiles of 128, four or five per workgroup,
+                             # ragged last tile
+    (131072, 1024, 65, 7),   # queries in registers, one valid row in the third wave
 ])
 def test_topk_parity(gpu, n_facts, dim, n_q, k):
     w = W.WORKLOADS["tiny"].scaled(name="topk", n_facts=n_facts, emb_dim=dim, n_req=n_q,
@@ -178,7 +182,9 @@ def test_topk_parity(gpu, n_facts, dim, n_q, k):
     try:
         q = W.query_embeddings(w)
         ids, sc = Hn.gpu_topk(st, q, k)
-        Hn.check_topk(q, st.emb, ids, sc, k)
+        # large stores: the oracle checks every third query and the last one
+        sel = None if n_facts < 100000 else sorted(set(range(0, n_q, 3)) | {n_q - 1})
+        Hn.check_topk(q, st.emb, ids, sc, k, queries=sel)
         ids2, sc2 = Hn.gpu_topk(st, q, k)
         assert np.array_equal(ids, ids2) and np.array_equal(sc, sc2)
     finally:
@@ -201,5 +207,62 @@ def test_topk_ties_and_self_match(gpu):
         assert ids[0].tolist() == [17, 300, 599]
         assert ids[2].tolist() == [17, 300, 599]
         assert ids[1, 0] == 5 and ids[3, 0] == 42
+    finally:
+        st.destroy()
+
+
+def test_topk_many_candidates_full_batch(gpu):
+    """A store where almost every fact shares one embedding: every fact of a
+    workgroup's tiles reaches the sample bound, so candidates overflow the
+    scan's staging area and the final selection gathers from the full list.
+    Equal scores go to the lower ids."""
+    w = W.WORKLOADS["tiny"].scaled(name="flat1024", n_facts=140001, emb_dim=1024, n_req=100,
+                                   len_dist=("uniform", 1, 1))
+    lens = W.fact_lengths(w)
+    emb = W.fact_embeddings(w)
+    distinct = [3, 1000, 70000, 139999]
+    common = emb[5].copy()
+    keep_rows = emb[distinct].copy()
+    emb[:] = common
+    emb[distinct] = keep_rows
+    desc, keep = Hn.K.make_desc(1, 2, 64, synth.F32, lens, 1024, -1, None, None, emb)
+    h = Hn.K.is_store_create(desc)
+    st = Hn.Store(w, lens, np.concatenate([[0], np.cumsum(lens)]), h, emb)
+    try:
+        q = W.query_embeddings(w)
+        ids, sc = Hn.gpu_topk(st, q, 10)
+        Hn.check_topk(q, st.emb, ids, sc, 10, queries=range(0, 100, 9))
+        for r in range(q.shape[0]):
+            shared = [int(f) for f in ids[r] if f not in distinct]
+            # facts of the shared embedding come in id order, the lowest first
+            lowest = [f for f in range(20) if f not in distinct][:len(shared)]
+            assert shared == lowest, f"query {r}: {shared}"
+    finally:
+        st.destroy()
+
+
+def test_topk_ties_full_batch_width_1024(gpu):
+    """Equal embeddings under the register-resident scan (100 queries x 1024):
+    equal scores are ordered by the lower id, a self-query ranks its copies
+    first."""
+    w = W.WORKLOADS["tiny"].scaled(name="ties1024", n_facts=140001, emb_dim=1024, n_req=100,
+                                   len_dist=("uniform", 1, 1))
+    lens = W.fact_lengths(w)
+    emb = W.fact_embeddings(w)
+    for dup in (300, 33000, 140000):
+        emb[dup] = emb[17]
+    desc, keep = Hn.K.make_desc(1, 2, 64, synth.F32, lens, 1024, -1, None, None, emb)
+    h = Hn.K.is_store_create(desc)
+    st = Hn.Store(w, lens, np.concatenate([[0], np.cumsum(lens)]), h, emb)
+    try:
+        q = W.query_embeddings(w)
+        q[0] = emb[17]
+        q[99] = emb[140000]
+        q[50] = emb[139999]
+        ids, sc = Hn.gpu_topk(st, q, 5)
+        assert ids[0, :4].tolist() == [17, 300, 33000, 140000]
+        assert ids[99, :4].tolist() == [17, 300, 33000, 140000]
+        assert ids[50, 0] == 139999
+        Hn.check_topk(q, st.emb, ids, sc, 5, queries=[0, 1, 50, 98, 99])
     finally:
         st.destroy()
