@@ -12,9 +12,11 @@
 // Design (gfx950; bf16 cache, head_dim 128).  One workgroup per (layer,
 // request, kv head) and group of up to 64 query rows (a row is a (query
 // token, query head of the group) pair).  The context is cut into 32-token
-// chunks taken round-robin by four chunk streams; each stream has one wave
-// per 32-row query tile (two waves when the group has more than 32 rows, so
-// eight waves, two per SIMD, each within 256 registers).  The queries are
+// chunks taken round-robin by the chunk streams (two when the group has
+// more than 32 rows, four otherwise); each stream has one wave per 32-row
+// query tile.  The two-tile kernel's four waves stay within 256 registers
+// and 69 KB of LDS, so two workgroups share a CU and one's query rotation
+// and final merge overlap the other's transfers.  The queries are
 // rotated at their positions, pre-scaled by log2(e) / sqrt(d) and split into
 // bf16 hi + lo once per workgroup; each wave keeps its tile's in registers.
 //
@@ -56,13 +58,17 @@
 #include "rope_math.h"
 
 // Chunk streams and ring slots per stream of the two-tile kernel (measured
-// on the 100-request Mistral-7B-shaped batch: 4 x 2 at 6.1 ms, 3 x 3 at 6.5,
+// on the 100-request Mistral-7B-shaped batch: 2 x 2 at 5.3-5.5 ms with two
+// workgroups per CU; with one workgroup per CU 4 x 2 at 6.0, 3 x 3 at 6.5,
 // 2 x 4 at 7.0).
 #ifndef IS_ATT_NS
-#define IS_ATT_NS 4
+#define IS_ATT_NS 2
 #endif
 #ifndef IS_ATT_NST
 #define IS_ATT_NST 2
+#endif
+#ifndef IS_ATT_MINW
+#define IS_ATT_MINW 2     // waves per SIMD the two-tile kernel's registers must allow
 #endif
 
 namespace is {
@@ -144,8 +150,8 @@ struct AttendSmem {
 // in 16 different bank groups.
 __device__ __forceinline__ int q_slot(int r, int j) { return r * 16 + (j ^ (r & 15)); }
 
-template <int QT, int NS, int NST>
-__global__ __launch_bounds__(QT * NS * 64) void attend_kernel(AttendLaunch a) {
+template <int QT, int NS, int NST, int MINW>
+__global__ __launch_bounds__(QT * NS * 64, MINW) void attend_kernel(AttendLaunch a) {
   constexpr int kStreams = NS;         // chunk streams
   constexpr int kStages = NST;         // ring slots per stream
   constexpr int kThreadsWG = QT * NS * 64;
@@ -391,7 +397,7 @@ __global__ __launch_bounds__(QT * NS * 64) void attend_kernel(AttendLaunch a) {
   }
   wait_vm<0>();   // no transfer may land in the LDS once it is reused below
 
-  // merge the four streams' states (per row tile)
+  // merge the streams' softmax states (per row tile)
   lsum += __shfl_xor(lsum, 32);
   lds_barrier();   // every wave is done with the ring (the union's other half)
   if (h == 0) {
@@ -526,9 +532,9 @@ hipError_t launch_attend(const AttendLaunch& in, hipStream_t stream) {
   const int64_t wgs = (a.n_units + 7) / 8 * 8 * a.groups;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   if (qt == 1)
-    hipLaunchKernelGGL((attend_kernel<1, 4, 2>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attend_kernel<1, 4, 2, 1>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((attend_kernel<2, IS_ATT_NS, IS_ATT_NST>), dim3((unsigned)wgs),
+    hipLaunchKernelGGL((attend_kernel<2, IS_ATT_NS, IS_ATT_NST, IS_ATT_MINW>), dim3((unsigned)wgs),
                        dim3(2 * IS_ATT_NS * 64), 0, stream, a);
   return hipGetLastError();
 }
