@@ -314,6 +314,71 @@ def host_tier_latency(torch, K, W, Hn, reps: int) -> dict:
             if t_mixed > t_hbm else None}
 
 
+def single_request_latency(torch, K, W, Hn, synth, reps: int) -> dict:
+    """One request with top-k retrieval on the tiny configuration (20 facts,
+    fp32, top-5) and on the Llama-3.1-8B-shaped store (10,000 facts, top-5,
+    Llama-3.1 RoPE scaling, the 98,304-block cache): wall time from the call
+    to the completed stream for the host path (is_topk, ids to the host,
+    is_inject) and the device path (is_retrieve_inject), and the inject
+    alone."""
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in ("tiny", "llama8b_single"):
+        w = W.WORKLOADS[name]
+        st = Hn.make_store(w, fill="host" if name == "tiny" else "gpu")
+        try:
+            q = torch.from_numpy(W.query_embeddings(w).view(np.int16)).cuda()
+            k = w.k
+            ids_d = torch.empty((1, k), dtype=torch.int32, device="cuda")
+            sc_d = torch.empty((1, k), dtype=torch.float32, device="cuda")
+            K.is_topk(st.handle, q, 1, k, ids_d, sc_d, stream)
+            req_off, flat = Hn.requests_from_ids(ids_d.cpu().numpy())
+            prefix = W.request_prefixes(w)
+            if name == "tiny":   # the configuration's shuffled 16-block table
+                bt = synth.permutation(w.seed, w.n_blocks)[None, :].copy()
+            else:
+                bt = Hn.block_tables_for(w, st.lens, req_off, flat, prefix)
+            cache = Hn.make_cache(w)
+            cdesc, rope = cache.desc, Hn.rope_of(w)
+            ids_h = torch.empty((1, k), dtype=torch.int32, pin_memory=True)
+            status = torch.full((1,), 1, dtype=torch.int32, device="cuda")
+            d_prefix = torch.from_numpy(prefix.astype(np.int32)).cuda()
+            d_bt = torch.from_numpy(np.ascontiguousarray(bt, np.int32)).cuda()
+
+            def host():
+                K.is_topk(st.handle, q, 1, k, ids_d, sc_d, stream)
+                ids_h.copy_(ids_d, non_blocking=True)
+                stream.synchronize()
+                K.is_inject(st.handle, req_off, ids_h.numpy().reshape(-1), prefix, bt, cdesc,
+                            rope, stream)
+                stream.synchronize()
+
+            def dev():
+                K.is_retrieve_inject(st.handle, q, 1, k, d_prefix, d_bt, cdesc, rope, status,
+                                     None, stream)
+                stream.synchronize()
+
+            def inject():
+                K.is_inject(st.handle, req_off, flat, prefix, bt, cdesc, rope, stream)
+                stream.synchronize()
+
+            t_host = median_ms(torch, host, reps)
+            t_dev = median_ms(torch, dev, reps)
+            assert int(status.item()) == 0, "device-side validation failed"
+            t_inj = median_ms(torch, inject, reps)
+            out[name] = {"tokens": int(st.lens[flat].sum()), "k": k,
+                         "host_path_ms": round(t_host, 4), "device_path_ms": round(t_dev, 4),
+                         "inject_ms": round(t_inj, 4)}
+            del cache
+        finally:
+            st.destroy()
+            torch.cuda.empty_cache()
+    out["note"] = ("median wall time per call including the final synchronize; tiny: 1 layer "
+                   "x 2 kv_heads x 64 fp32, 20 facts; llama8b_single: 32 x 8 x 128 bf16, "
+                   "10,000 facts, 98,304 x 16-slot cache")
+    return out
+
+
 def ingest_rate(torch, K, W, synth, reps: int, n_batch: int = 512, window: int = 32) -> dict:
     """Store ingest on the Mistral-7B geometry: appends of n_batch facts
     (the workload's lognormal lengths) packed from context-window encodings
@@ -466,6 +531,8 @@ def main() -> int:
                     help="only run the top-k over 1M x 1024 embeddings (for profiling)")
     ap.add_argument("--skip-topk-1m", action="store_true",
                     help="leave out the top-k over 1M x 1024 embeddings")
+    ap.add_argument("--skip-single", action="store_true",
+                    help="skip the single-request latency of the tiny and Llama-8B configurations")
     ap.add_argument("--skip-host-tier", action="store_true",
                     help="leave out the single-request host-tier latency")
     ap.add_argument("--skip-ingest", action="store_true",
@@ -614,6 +681,12 @@ def main() -> int:
     st.destroy()
     del cache
     torch.cuda.empty_cache()
+    single = None
+    if not args.skip_single:
+        log("single requests: tiny and Llama-3.1-8B-shaped configurations, top-5")
+        single = single_request_latency(torch, K, W, Hn, synth, max(args.steps, 5))
+        log(f"single request: tiny {single['tiny']['device_path_ms']:.3f} ms, llama8b "
+            f"{single['llama8b_single']['device_path_ms']:.3f} ms (device path)")
     host_tier = None
     if not args.skip_host_tier:
         log("host tier: one request on the Qwen3-14B-shaped store, half pinned on the host")
@@ -682,6 +755,7 @@ def main() -> int:
         "topk_1m": topk_1m,
         "device_path": dev,
         "attend": attend,
+        "single_request": single,
         "host_tier": host_tier,
         "ingest": ingest,
         "copy_GBps": round(copy_gbps, 1),

@@ -1,6 +1,7 @@
 """Shared GPU-test, smoke and bench plumbing: builds stores and caches from
 the seeded generator, calls the library through its C ABI, and compares with
-the oracle.
+the oracle.  The oracle is imported only by the checking helpers, so the
+bench's GPU legs, which use the builders, never load it.
 
 Tolerances (what the GPU path must meet against the oracle):
   V rows, slot placement, untouched cache bytes   bit-exact
@@ -22,7 +23,6 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 import kv_cache_injection_is_amd as K  # noqa: E402
-import oracle  # noqa: E402
 import synth  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
@@ -60,6 +60,7 @@ def rope_of(w: W.Workload) -> "K.is_rope":
 
 
 def oracle_freqs(w: W.Workload) -> np.ndarray:
+    import oracle
     return oracle.rope_freqs(w.head_dim, w.theta, w.scaling, w.rope_factor, w.rope_low,
                              w.rope_high, w.rope_orig)
 
@@ -197,6 +198,7 @@ def check_topk(q_bits, e_bits, gpu_ids, gpu_scores, k, queries=None):
     """Checks the GPU top-k against the exact fp64 oracle (see module doc)."""
     qsel = list(range(q_bits.shape[0])) if queries is None else list(queries)
     # the oracle's (k+1)-th score bounds what may enter at the boundary
+    import oracle
     o_ids1, o_sc1 = oracle.topk(q_bits[qsel], e_bits, min(k + 1, e_bits.shape[0]))
     o_ids, o_sc = o_ids1[:, :k], o_sc1[:, :k]
     for n, qi in enumerate(qsel):
@@ -279,6 +281,7 @@ def oracle_blocks(w: W.Workload, lens, req_off, flat_ids, prefix, bt, blocks, la
     else:
         strides = (m * B * H * d, H * B * d, d, B * d)
     ids_c = np.array([remap[int(f)] for f in flat_ids], dtype=np.int32)
+    import oracle
     oracle.inject(L, H, d, w.dtype, Kh, Vh, sub_off, req_off, ids_c, prefix, bt_c, B, m,
                   kc, vc, strides, oracle_freqs(w))
     return kc, vc
@@ -288,6 +291,7 @@ def touched_mask(w: W.Workload, lens, req_off, flat_ids, prefix, bt, blocks, lay
     """Byte mask [m][B*H*d*es] of the elements the oracle writes (per layer
     the same), from the oracle's slot map."""
     B, H, d, es = w.block_size, w.n_kv_heads, w.head_dim, w.elem_size
+    import oracle
     slots = oracle.token_slots(req_off, flat_ids, lens, prefix, bt, B)
     bidx = {int(b): i for i, b in enumerate(blocks)}
     mask = np.zeros((len(blocks), B, H, d), dtype=bool) if layout == "NHD" else \

@@ -5,6 +5,7 @@ cache untouched on every failure."""
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from synth import workloads as W
 from tests import harness as Hn
@@ -71,7 +72,7 @@ def test_device_path_matches_host_path_and_oracle(gpu, hbm_half):
         n, err = Hn.check_inject_blocks(c_dev, lens, req_off, flat, prefix, bt,
                                         Hn.blocks_of(bt, range(w.n_req)))
         Hn.log(f"  {n} K elements vs oracle, max err {err:.3g}")
-        Hn.check_untouched(c_dev, Hn.oracle.token_slots(req_off, flat, lens, prefix, bt,
+        Hn.check_untouched(c_dev, oracle.token_slots(req_off, flat, lens, prefix, bt,
                                                         w.block_size))
     finally:
         st.destroy()
