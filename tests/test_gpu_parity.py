@@ -173,6 +173,8 @@ def test_inject_invalid_call_writes_nothing(gpu):
                              # more): 1,094 tiles of 128, four or five per workgroup,
                              # ragged last tile
     (131072, 1024, 65, 7),   # queries in registers, one valid row in the third wave
+    (131500, 1024, 130, 64), # 128 queries in registers (every wave full), the last two
+                             # by the staged scan; k at its maximum
 ])
 def test_topk_parity(gpu, n_facts, dim, n_q, k):
     w = W.WORKLOADS["tiny"].scaled(name="topk", n_facts=n_facts, emb_dim=dim, n_req=n_q,
