@@ -26,14 +26,21 @@
 // fact scores identically in both.
 //
 // Scan layout.  The store keeps the embeddings tile-blocked (see kernels.h):
-// every 256-fact x 64-dim block is one contiguous 32 KB span.  A persistent
-// workgroup (4 waves, one per SIMD) streams its tiles' blocks, and the
-// matching 128 x 64 query chunk, from memory straight into a 3-stage LDS
-// ring with global_load_lds_dwordx4 (no registers on the way).  Each wave
-// owns 64 facts of the tile (two 32-row tiles of v_mfma_f32_32x32x16_f16,
-// fp32 accumulation) against all 128 queries, and loads those 64 rows
-// itself, so it refills its part of a buffer without waiting for the other
-// waves: the fact rows of three chunks can be in flight while it waits.
+// every 256-fact x 64-dim block is one contiguous 32 KB span.  Persistent
+// workgroups (4 waves, one per SIMD, one workgroup per CU) stream their
+// tiles' blocks from memory straight into an LDS ring with
+// global_load_lds_dwordx4 (no registers on the way); v_mfma_f32_32x32x16_f16
+// forms the scores with fp32 accumulation.  Two variants:
+//   topk_scan     each wave owns 64 facts of a 256-fact tile against every
+//                 query tile the launch fills; the query chunk is staged
+//                 with the fact block in a 3-stage ring, and a wave refills
+//                 its own fact rows without waiting for the other waves;
+//   topk_scan_qr  full batches at width 1024 over large stores: each wave
+//                 keeps its 32 query rows in registers for the whole launch
+//                 and scores every fact of a 128-fact tile, the ring (eight
+//                 16 KB stages, seven in flight) holds fact rows only, and
+//                 candidates are staged in LDS until the loop ends (see
+//                 below).
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
