@@ -322,14 +322,16 @@ __global__ __launch_bounds__(QT * NS * 64, MINW) void attend_kernel(AttendLaunch
     }
     // online softmax (base 2); P split for the second product
     float sv[16];
-    float mx = -INFINITY;
-    const bool tail = c0 + kChunk > n_ctx;   // the last, partial chunk
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ti = c0 + 8 * (i / 4) + 4 * h + (i % 4);
-      sv[i] = (!tail || ti < n_ctx) ? st[i] : -INFINITY;
-      mx = fmaxf(mx, sv[i]);
+    for (int i = 0; i < 16; ++i) sv[i] = st[i];
+    if (c0 + kChunk > n_ctx) {   // the last, partial chunk (a uniform branch)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (c0 + 8 * (i / 4) + 4 * h + (i % 4) >= n_ctx) sv[i] = -INFINITY;
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // Lazy rescaling: the reference m only moves when some row's maximum
     // passes it by more than 8 (a factor 256 in the weights); until then
