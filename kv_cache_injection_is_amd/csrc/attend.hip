@@ -75,6 +75,8 @@ namespace is {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
@@ -96,19 +98,18 @@ __device__ __forceinline__ float bf16_value(unsigned short b) {
   return __uint_as_float((unsigned)b << 16);
 }
 
-// Splits 8 floats into bf16 hi and lo parts (x ~= hi + lo).
+// Splits 8 floats into bf16 hi and lo parts (x ~= hi + lo), two values per
+// conversion (round to nearest even, as one at a time).
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-  unsigned short h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = bf16_bits(x[e]);
-    l[e] = bf16_bits(x[e] - bf16_value(h[e]));
-  }
   u32x4 hv, lv;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    hv[w] = (unsigned)h[2 * w] | ((unsigned)h[2 * w + 1] << 16);
-    lv[w] = (unsigned)l[2 * w] | ((unsigned)l[2 * w + 1] << 16);
+    const float2v pair = {x[2 * w], x[2 * w + 1]};
+    const unsigned hp = __builtin_bit_cast(unsigned, __builtin_convertvector(pair, bf16x2));
+    const float2v rest = {x[2 * w] - __uint_as_float(hp << 16),
+                          x[2 * w + 1] - __uint_as_float(hp & 0xFFFF0000u)};
+    hv[w] = hp;
+    lv[w] = __builtin_bit_cast(unsigned, __builtin_convertvector(rest, bf16x2));
   }
   hi = __builtin_bit_cast(bf16x8, hv);
   lo = __builtin_bit_cast(bf16x8, lv);
