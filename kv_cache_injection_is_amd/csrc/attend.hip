@@ -219,14 +219,21 @@ __global__ __launch_bounds__(QT * NS * 64, MINW) void attend_kernel(AttendLaunch
     const int r_lo = (int)(uint32_t)rowe, r_hi = (int)(rowe >> 32);
     const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(ring0 + (uint32_t)((s * kStreams + sid) * kStageBytes)));
+    // every row offset first, then the transfers: the asm transfers order
+    // memory, so a shuffle placed between two of them would wait alone
+    int64_t rj[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = 4 * j + tq;
-      const int64_t rj = (int64_t)(((uint64_t)(uint32_t)__shfl(r_hi, t) << 32) |
-                                   (uint32_t)__shfl(r_lo, t));
-      if (QT == 1 || rt == 0) dma16(kc + rj * 2 + ((pos16 ^ (t & 15)) << 4), base + j * 1024);
+      rj[j] = (int64_t)(((uint64_t)(uint32_t)__shfl(r_hi, t) << 32) | (uint32_t)__shfl(r_lo, t));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = 4 * j + tq;
+      if (QT == 1 || rt == 0)
+        dma16(kc + rj[j] * 2 + ((pos16 ^ (t & 15)) << 4), base + j * 1024);
       if (QT == 1 || rt == 1)
-        dma16(vc + rj * 2 + ((pos16 ^ (4 * tq)) << 4), base + kTileBytes + j * 1024);
+        dma16(vc + rj[j] * 2 + ((pos16 ^ (4 * tq)) << 4), base + kTileBytes + j * 1024);
     }
   };
 
