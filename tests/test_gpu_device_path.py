@@ -148,3 +148,33 @@ def test_device_path_many_requests(gpu):
                                    Hn.blocks_of(bt, range(a, b + 1)))
     finally:
         st.destroy()
+
+
+def test_device_path_large_index(gpu):
+    """100 requests x top-50 over 140,001 one-token facts with 1024-dim
+    embeddings: the device path runs the register-resident top-k scan (the
+    host path's is_topk the same kernel); ids, status and every cache byte
+    equal the host path's, the ids pass the oracle on sampled queries."""
+    import torch
+    w = W.WORKLOADS["tiny"].scaled(name="device_large", n_layers=2, n_kv_heads=1,
+                                   head_dim=128, dtype=synth.BF16, n_facts=140001,
+                                   len_dist=("uniform", 1, 1), emb_dim=1024, n_req=100, k=50,
+                                   block_size=16, n_blocks=600, prefix=(0, 16), theta=1e6,
+                                   scaling="none")
+    st = Hn.make_store(w)
+    try:
+        q, ids, req_off, flat, prefix, bt = _problem(st, w, w.n_req, w.k)
+        c_dev = Hn.make_cache(w)
+        c_host = Hn.make_cache(w)
+        status, d_ids = _device_call(st, w, q, w.k, prefix, bt, c_dev)
+        assert status == 0
+        assert np.array_equal(d_ids, ids)
+        Hn.gpu_inject(st, c_host, req_off, flat, prefix, bt)
+        torch.cuda.synchronize()
+        assert torch.equal(c_dev.k, c_host.k) and torch.equal(c_dev.v, c_host.v)
+        _, sc = Hn.gpu_topk(st, q, w.k)
+        Hn.check_topk(q, st.emb, ids, sc, w.k, queries=[0, 33, 66, 99])
+        Hn.check_inject_blocks(c_dev, st.lens, req_off[:3], flat[:req_off[2]], prefix[:2],
+                               bt[:2], Hn.blocks_of(bt, range(2)))
+    finally:
+        st.destroy()

@@ -175,6 +175,8 @@ def test_inject_invalid_call_writes_nothing(gpu):
     (131072, 1024, 65, 7),   # queries in registers, one valid row in the third wave
     (131500, 1024, 130, 64), # 128 queries in registers (every wave full), the last two
                              # by the staged scan; k at its maximum
+    (131100, 992, 70, 9),    # width 992: queries padded to 1024 through the scratch
+                             # copy, then held in registers
 ])
 def test_topk_parity(gpu, n_facts, dim, n_q, k):
     w = W.WORKLOADS["tiny"].scaled(name="topk", n_facts=n_facts, emb_dim=dim, n_req=n_q,
