@@ -541,8 +541,9 @@ def main() -> int:
                     help="only run the store-ingest rate (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs the path on a single MI355X; "
-              "see DESIGN.md for how it would shard", file=sys.stderr)
+        print("bench.py measures one GPU: the path runs on a single MI355X (across GPUs it "
+              "would shard the store by kv head, or the requests, with no exchange)",
+              file=sys.stderr)
         return 2
 
     import torch
