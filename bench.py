@@ -235,7 +235,7 @@ def host_tier_latency(torch, K, W, Hn, reps: int) -> dict:
     facts in pinned host memory: latency of the host path, of the device
     path and of the inject alone; the same inject with every host-tier fact
     swapped for an HBM fact of the same length (the cost of the offload);
-    and the pinned host-to-device copy rate of the same box."""
+    and the pinned host-to-device copy rate of the same machine."""
     w = W.WORKLOADS["qwen3_14b_offload"]
     lens = W.fact_lengths(w)
     n_hbm = int(len(lens) * (1 - w.host_fraction))
@@ -696,7 +696,7 @@ def main() -> int:
             log(f"host tier: inject {host_tier['inject_ms']:.3f} ms "
                 f"(all-HBM {host_tier['inject_all_hbm_ms']:.3f} ms), host path "
                 f"{host_tier['host_path_ms']:.3f} ms, device path {host_tier['device_path_ms']:.3f} ms")
-        except Exception as e:     # a box that cannot pin the tier
+        except Exception as e:     # a host that cannot pin the tier
             host_tier = {"error": f"{type(e).__name__}: {e}"}
             log(f"host tier skipped: {host_tier['error']}")
     ingest = None

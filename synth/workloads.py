@@ -86,7 +86,7 @@ WORKLOADS = {
     # Qwen2.5-7B-shaped: 1M facts, half of them (the upper ids) in pinned host
     # memory, exact top-50 over 1M embeddings for 100 queries, block 16.
     # Lengths 1-3 tokens (mean 2): the host half is then 57 GB, within the
-    # 64 GiB of host memory the test boxes can pin (4-12 tokens would need
+    # 64 GiB of host memory an MI355X host here can pin (4-12 tokens would need
     # 229 GB pinned).
     "qwen7b_offload": Workload("qwen7b_offload", 28, 4, 128, BF16, 1_000_000,
                                ("uniform", 1, 3), 1024, 100, 50, "topk",
