@@ -340,7 +340,9 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
   }
 }
 
-// Scan variant for full query batches (65..128 queries) at width 1024.
+// Scan variant for full query batches (65..128 queries) at width 1024 over
+// stores of kResidentMinFacts or more (below it a workgroup's chunks are too
+// few to fill the deeper ring).
 // The query rows are the same for every tile, so instead of re-staging them
 // through LDS for every chunk, each wave keeps its own 32 query rows -- all
 // 1024 dims, 256 registers per lane -- for the whole launch, and the LDS
