@@ -314,6 +314,43 @@ def host_tier_latency(torch, K, W, Hn, reps: int) -> dict:
             if t_mixed > t_hbm else None}
 
 
+def llama_batch_inject(torch, K, W, Hn, st, stream, reps: int) -> dict:
+    """The Llama-3.1-8B-shaped batch on the same store: 100 requests x 50
+    distinct facts drawn Zipf(1.1) in draw order, prefixes U[16,256], block 16,
+    a fresh 98,304-block cache; back-to-back is_inject calls timed with HIP
+    events on the stream."""
+    w = W.WORKLOADS["llama8b_batch"]
+    ids = W.zipf_fact_ids(w)
+    req_off, flat = Hn.requests_from_ids(ids)
+    prefix = W.request_prefixes(w)
+    bt = Hn.block_tables_for(w, st.lens, req_off, flat, prefix)
+    cache = Hn.make_cache(w)
+    cdesc, rope = cache.desc, Hn.rope_of(w)
+
+    def call():
+        K.is_inject(st.handle, req_off, flat, prefix, bt, cdesc, rope, stream)
+
+    call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tokens = int(st.lens[flat].sum())
+    moved = tokens * w.token_bytes * 4   # K and V, read and written
+    del cache
+    return {"workload": "llama8b_batch: 32 layers x 8 kv_heads x 128 bf16, 10,000 facts "
+                        "(lengths 12-64), 100 requests x 50 Zipf(1.1) facts, block 16, "
+                        "RoPE theta 5e5 with Llama-3.1 scaling",
+            "tokens": tokens, "inject_ms": round(ms, 4),
+            "tokens_per_s": round(tokens / (ms / 1e3), 1),
+            "GBps": round(moved / (ms / 1e3) / 1e9, 1),
+            "frac_of_8TBps": round(moved / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": moved}
+
+
 def single_request_latency(torch, K, W, Hn, synth, reps: int) -> dict:
     """One request with top-k retrieval on the tiny configuration (20 facts,
     fp32, top-5) and on the Llama-3.1-8B-shaped store (10,000 facts, top-5,
@@ -370,12 +407,16 @@ def single_request_latency(torch, K, W, Hn, synth, reps: int) -> dict:
                          "host_path_ms": round(t_host, 4), "device_path_ms": round(t_dev, 4),
                          "inject_ms": round(t_inj, 4)}
             del cache
+            if name == "llama8b_single":
+                torch.cuda.empty_cache()
+                out["llama8b_batch"] = llama_batch_inject(torch, K, W, Hn, st, stream, reps)
         finally:
             st.destroy()
             torch.cuda.empty_cache()
-    out["note"] = ("median wall time per call including the final synchronize; tiny: 1 layer "
-                   "x 2 kv_heads x 64 fp32, 20 facts; llama8b_single: 32 x 8 x 128 bf16, "
-                   "10,000 facts, 98,304 x 16-slot cache")
+    out["note"] = ("tiny, llama8b_single: median wall time per call including the final "
+                   "synchronize; tiny: 1 layer x 2 kv_heads x 64 fp32, 20 facts; "
+                   "llama8b_single: 32 x 8 x 128 bf16, 10,000 facts, 98,304 x 16-slot cache; "
+                   "llama8b_batch: HIP events around back-to-back is_inject calls")
     return out
 
 
@@ -687,7 +728,9 @@ def main() -> int:
         log("single requests: tiny and Llama-3.1-8B-shaped configurations, top-5")
         single = single_request_latency(torch, K, W, Hn, synth, max(args.steps, 5))
         log(f"single request: tiny {single['tiny']['device_path_ms']:.3f} ms, llama8b "
-            f"{single['llama8b_single']['device_path_ms']:.3f} ms (device path)")
+            f"{single['llama8b_single']['device_path_ms']:.3f} ms (device path); llama8b batch "
+            f"inject {single['llama8b_batch']['inject_ms']:.3f} ms "
+            f"({single['llama8b_batch']['GBps']:.0f} GB/s)")
     host_tier = None
     if not args.skip_host_tier:
         log("host tier: one request on the Qwen3-14B-shaped store, half pinned on the host")
