@@ -420,6 +420,71 @@ def single_request_latency(torch, K, W, Hn, synth, reps: int) -> dict:
     return out
 
 
+def offload_batch(torch, K, W, Hn, reps: int) -> dict:
+    """The Qwen2.5-7B-shaped workload: 1M facts, the upper half in pinned host
+    memory; exact top-50 for 100 queries, then inject of those 100 x 50 facts
+    (about half of them read over PCIe by the kernel).  Times the top-k, the
+    inject (HIP events around back-to-back calls) and the whole step."""
+    w = W.WORKLOADS["qwen7b_offload"]
+    lens = W.fact_lengths(w)
+    n_hbm = int(len(lens) * (1 - w.host_fraction))
+    budget = int(lens[:n_hbm].sum()) * w.token_bytes * 2
+    stream = torch.cuda.current_stream()
+    st = Hn.make_store(w, lens, hbm_budget=budget)
+    try:
+        q = torch.from_numpy(W.query_embeddings(w).view(np.int16)).cuda()
+        n, k = w.n_req, w.k
+        ids_d = torch.empty((n, k), dtype=torch.int32, device="cuda")
+        sc_d = torch.empty((n, k), dtype=torch.float32, device="cuda")
+        ids_h = torch.empty((n, k), dtype=torch.int32, pin_memory=True)
+        K.is_topk(st.handle, q, n, k, ids_d, sc_d, stream)
+        req_off, flat = Hn.requests_from_ids(ids_d.cpu().numpy())
+        prefix = W.request_prefixes(w)
+        bt = Hn.block_tables_for(w, st.lens, req_off, flat, prefix)
+        cache = Hn.make_cache(w)
+        cdesc, rope = cache.desc, Hn.rope_of(w)
+
+        def inject_call():
+            K.is_inject(st.handle, req_off, flat, prefix, bt, cdesc, rope, stream)
+
+        inject_call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            inject_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_inj = e0.elapsed_time(e1) / reps
+
+        def step():
+            K.is_topk(st.handle, q, n, k, ids_d, sc_d, stream)
+            ids_h.copy_(ids_d, non_blocking=True)
+            stream.synchronize()
+            K.is_inject(st.handle, req_off, ids_h.numpy().reshape(-1), prefix, bt, cdesc, rope,
+                        stream)
+            stream.synchronize()
+
+        t_step = median_ms(torch, step, reps)
+        tokens = int(lens[flat].sum())
+        host_tokens = int(lens[flat[flat >= n_hbm]].sum())
+        del cache
+    finally:
+        st.destroy()
+        torch.cuda.empty_cache()
+    moved = tokens * w.token_bytes * 4
+    return {"workload": "qwen7b_offload: 28 layers x 4 kv_heads x 128 bf16, 1,000,000 facts "
+                        "(lengths 1-3), the upper half pinned on the host; 100 requests x "
+                        "top-50 over 1M x 1024 fp16 embeddings, block 16",
+            "tokens": tokens, "host_tier_tokens": host_tokens,
+            "host_tier_bytes": host_tokens * w.token_bytes * 2,
+            "inject_ms": round(t_inj, 4), "step_ms": round(t_step, 4),
+            "tokens_per_s": round(tokens / (t_step / 1e3), 1),
+            "inject_GBps": round(moved / (t_inj / 1e3) / 1e9, 1),
+            "host_tier_GBps": round(host_tokens * w.token_bytes * 2 / (t_inj / 1e3) / 1e9, 1),
+            "note": "inject_GBps counts K+V read and written for every token; the host-tier "
+                    "share of the reads crosses PCIe inside the same launch"}
+
+
 def ingest_rate(torch, K, W, synth, reps: int, n_batch: int = 512, window: int = 32) -> dict:
     """Store ingest on the Mistral-7B geometry: appends of n_batch facts
     (the workload's lognormal lengths) packed from context-window encodings
@@ -742,6 +807,16 @@ def main() -> int:
         except Exception as e:     # a host that cannot pin the tier
             host_tier = {"error": f"{type(e).__name__}: {e}"}
             log(f"host tier skipped: {host_tier['error']}")
+    offload = None
+    if not args.skip_host_tier:
+        log("offload batch: 1M-fact Qwen2.5-shaped store, half pinned on the host")
+        try:
+            offload = offload_batch(torch, K, W, Hn, max(args.steps, 5))
+            log(f"offload batch: step {offload['step_ms']:.3f} ms, inject {offload['inject_ms']:.3f} "
+                f"ms ({offload['host_tier_bytes'] / 1e9:.2f} GB over PCIe)")
+        except Exception as e:     # a host that cannot pin the tier
+            offload = {"error": f"{type(e).__name__}: {e}"}
+            log(f"offload batch skipped: {offload['error']}")
     ingest = None
     if not args.skip_ingest:
         log("store ingest: appends from window encodings")
@@ -801,6 +876,7 @@ def main() -> int:
         "attend": attend,
         "single_request": single,
         "host_tier": host_tier,
+        "offload_batch": offload,
         "ingest": ingest,
         "copy_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
