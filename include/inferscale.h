@@ -28,7 +28,13 @@
  *     stay valid until the work enqueued on `stream` has completed;
  *   - `stream` is a hipStream_t (NULL = the default stream);
  *   - validation completes before anything is enqueued: on error nothing
- *     is written anywhere (all or nothing).
+ *     is written anywhere (all or nothing);
+ *   - thread safety: each store has a lock that every call taking the
+ *     store holds while it reads or changes the store's tables, so calls
+ *     from several host threads are safe; the device work of a call is
+ *     ordered only on its own stream, so work that changes a store
+ *     (append, update) must be ordered by the caller against work on other
+ *     streams that reads the same facts.
  */
 #ifndef INFERSCALE_H
 #define INFERSCALE_H
@@ -149,6 +155,9 @@ typedef struct {
 } is_store_info;
 
 /*
+ * (Online phase, pre-RoPE storage: every fact's keys captured before RoPE
+ * and its raw values, held on the GPU; Results, scalability: the part that
+ * does not fit in HBM is offloaded to host DRAM.)
  * Creates a store: allocates device memory for the facts that fit the HBM
  * budget (and pinned host memory for the rest) plus the fp16 embedding
  * matrix, and copies the optional sources.  The library owns the memory;
@@ -160,6 +169,8 @@ typedef struct {
 int is_store_create(const is_store_desc* desc, is_store** out);
 
 /*
+ * (Offline phase: the facts' encodings are computed ahead of serving and
+ * written into the store.)
  * Fills facts [first_fact, first_fact + n_facts) from K/V sources laid out
  * like the store (those facts' blocks back to back) and, when emb is not
  * NULL, their embedding rows.  src_on_device = 1 means the sources are
@@ -171,10 +182,14 @@ int is_store_load(is_store* s, int64_t first_fact, int64_t n_facts,
                   const void* k, const void* v, const uint16_t* emb,
                   int src_on_device);
 
-/* Placement summary.  Errors: IS_ERR_INVALID_ARG. */
+/* Placement summary (Results, scalability: HBM and host-DRAM tiers).
+ * Errors: IS_ERR_INVALID_ARG. */
 int is_store_get_info(const is_store* s, is_store_info* out);
 
 /*
+ * (Contributions, GPU-native system design: retrieval over an index that
+ * stays on the GPU; the pages do not describe the index, and this exact
+ * search stands in for it.)
  * Exact top-k inner-product search: for each query q (device
  * q_f16[n_q][emb_dim], fp16 bits) the k facts with the largest
  * <q, E[f]> (fp16 products, fp32 accumulation on the matrix cores), written
@@ -188,6 +203,10 @@ int is_topk(const is_store* s, const uint16_t* q_f16, int32_t n_q, int32_t k,
             int32_t* ids, float* scores, void* stream);
 
 /*
+ * (Online phase: the retrieved facts are composed into one contiguous
+ * segment, every stored key gets the RoPE rotation of its new serving
+ * position -- dynamic rotation, exact by Theorem 6 -- and the K/V are
+ * scatter-copied into the engine's paged KV cache.)
  * Retrieve-and-inject for a batch of requests.
  *   req_off[n_req+1]   host; request r uses fact_ids[req_off[r]..req_off[r+1])
  *   fact_ids[]         host; facts in segment order (a repeat is allowed and
@@ -350,6 +369,8 @@ int is_attend(const is_store* s, const is_cache* cache, const is_rope* rope, int
               int32_t max_blocks, float* out, void* stream);
 
 /*
+ * (Online phase: composition of the retrieved facts into one segment after
+ * the prefix, as for is_inject.)
  * The host half of is_inject on its own: validation and composition
  * against a store description (no store, no GPU).  Returns the status
  * is_inject would return for the same arguments before any device work,
@@ -363,12 +384,14 @@ int is_inject_check(const is_store_desc* desc, int32_t n_req,
                     const is_rope* rope, int64_t* n_tokens);
 
 /*
+ * (Offline phase: the store lives across serving; this ends its life.)
  * Frees the store's device and host memory.  The caller must have
  * completed all streams that use it.  NULL is a no-op.
  */
 int is_store_destroy(is_store* s);
 
-/* Description of the calling thread's last error (empty if none). */
+/* Description of the calling thread's last error (empty if none); a
+ * library convention, no passage of the pages. */
 const char* is_last_error(void);
 
 #ifdef __cplusplus

@@ -355,6 +355,7 @@ IS_EXPORT int is_store_load(is_store* s, int64_t first, int64_t n, const void* k
                             const void* v, const uint16_t* emb, int src_on_device) {
   is::clear_error();
   if (s == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  std::lock_guard<std::mutex> lock(s->mu);
   if (first < 0 || n < 0 || first + n > s->n_facts)
     return fail(IS_ERR_INVALID_ARG, "fact range outside the store");
   if (emb != nullptr && s->emb_dim == 0)
@@ -413,6 +414,7 @@ IS_EXPORT int is_store_load(is_store* s, int64_t first, int64_t n, const void* k
 IS_EXPORT int is_store_get_info(const is_store* s, is_store_info* out) {
   is::clear_error();
   if (s == nullptr || out == nullptr) return fail(IS_ERR_INVALID_ARG, "null argument");
+  std::lock_guard<std::mutex> lock(const_cast<is_store*>(s)->mu);
   out->n_facts = s->n_facts;
   out->n_hbm_facts = s->n_hbm;
   out->hbm_kv_bytes = (int64_t)s->fact_bytes(0, s->n_hbm) * 2;
@@ -454,6 +456,8 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
   is::clear_error();
   if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
   is_store* s = const_cast<is_store*>(cs);
+  // planning reads the fact tables, which appends and removals change
+  std::lock_guard<std::mutex> lock(s->mu);
   thread_local std::vector<is::WorkItem> items;
   thread_local std::vector<float> g;
   int64_t n_tokens = 0;
@@ -484,7 +488,6 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
   const size_t g_bytes = align256(g.size() * sizeof(float));
   const size_t total = items_bytes + bt_bytes + g_bytes;
   DeviceGuard guard(s->device);
-  std::lock_guard<std::mutex> lock(s->mu);
   Slot* sl = nullptr;
   rc = acquire_slot(s, total, &sl);
   if (rc != IS_OK) return rc;
@@ -522,45 +525,72 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
   return IS_OK;
 }
 
-IS_EXPORT int is_topk(const is_store* cs, const uint16_t* q, int32_t n_q, int32_t k,
-                      int32_t* ids, float* scores, void* stream) {
-  is::clear_error();
-  if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
-  is_store* s = const_cast<is_store*>(cs);
+namespace {
+
+// Checks of a top-k call against its store (caller holds s->mu).  Sets
+// *nothing = true when there is nothing to do (n_q == 0).
+int check_topk_call(const is_store* s, const uint16_t* q, int32_t n_q, int32_t k,
+                    const int32_t* ids, const float* scores, bool* nothing) {
+  *nothing = false;
   if (s->emb_dim == 0 || s->emb == nullptr)
     return fail(IS_ERR_UNSUPPORTED, "store has no embedding index");
   if (n_q < 0) return fail(IS_ERR_INVALID_ARG, "n_q < 0");
   if (k < 1 || k > s->n_facts) return fail(IS_ERR_INVALID_ARG, "k must be in [1, n_facts]");
   if (k > 64) return fail(IS_ERR_UNSUPPORTED, "k > 64");
-  if (n_q == 0) return IS_OK;
+  if (n_q == 0) {
+    *nothing = true;
+    return IS_OK;
+  }
   if (q == nullptr || ids == nullptr || scores == nullptr)
     return fail(IS_ERR_INVALID_ARG, "null query or output pointer");
   if (((uintptr_t)q & 15u) != 0) return fail(IS_ERR_ALIGN, "queries must be 16-byte aligned");
+  return IS_OK;
+}
+
+// The launch of queries [q0, q0 + nq) (nq <= 128) with its scratch at `p`,
+// laid out as `lay`.
+is::TopkLaunch topk_launch_of(const is_store* s, const uint16_t* q, int32_t q0, int32_t nq,
+                              int32_t k, char* p, const is::TopkScratch& lay, int32_t* ids,
+                              float* scores) {
+  is::TopkLaunch a{};
+  a.emb = s->emb;
+  a.q = q + (int64_t)q0 * s->emb_dim;
+  a.n_facts = s->n_facts;
+  a.emb_dim = s->emb_dim;
+  a.n_q = nq;
+  a.k = k;
+  a.q_pad = reinterpret_cast<uint16_t*>(p + lay.q_off);
+  a.gmax = reinterpret_cast<uint32_t*>(p + lay.gmax_off);
+  a.tau = reinterpret_cast<float*>(p + lay.tau_off);
+  a.count = reinterpret_cast<uint32_t*>(p + lay.count_off);
+  a.cand = reinterpret_cast<uint64_t*>(p + lay.cand_off);
+  a.ids = ids + (int64_t)q0 * k;
+  a.scores = scores + (int64_t)q0 * k;
+  return a;
+}
+
+}  // namespace
+
+IS_EXPORT int is_topk(const is_store* cs, const uint16_t* q, int32_t n_q, int32_t k,
+                      int32_t* ids, float* scores, void* stream) {
+  is::clear_error();
+  if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  is_store* s = const_cast<is_store*>(cs);
+  std::lock_guard<std::mutex> lock(s->mu);   // n_facts and the index move under removals
+  bool nothing = false;
+  int rc = check_topk_call(s, q, n_q, k, ids, scores, &nothing);
+  if (rc != IS_OK || nothing) return rc;
   DeviceGuard guard(s->device);
-  std::lock_guard<std::mutex> lock(s->mu);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // Queries go in groups of up to 128 (one scan launch each).
   for (int32_t q0 = 0; q0 < n_q; q0 += 128) {
     const int32_t nq = std::min<int32_t>(128, n_q - q0);
     const is::TopkScratch lay = is::topk_scratch(s->n_facts, nq, s->emb_dim);
     Slot* sl = nullptr;
-    int rc = acquire_topk_slot(s, lay.bytes, &sl);
+    rc = acquire_topk_slot(s, lay.bytes, &sl);
     if (rc != IS_OK) return rc;
-    char* p = static_cast<char*>(sl->dev);
-    is::TopkLaunch a{};
-    a.emb = s->emb;
-    a.q = q + (int64_t)q0 * s->emb_dim;
-    a.n_facts = s->n_facts;
-    a.emb_dim = s->emb_dim;
-    a.n_q = nq;
-    a.k = k;
-    a.q_pad = reinterpret_cast<uint16_t*>(p + lay.q_off);
-    a.gmax = reinterpret_cast<uint32_t*>(p + lay.gmax_off);
-    a.tau = reinterpret_cast<float*>(p + lay.tau_off);
-    a.count = reinterpret_cast<uint32_t*>(p + lay.count_off);
-    a.cand = reinterpret_cast<uint64_t*>(p + lay.cand_off);
-    a.ids = ids + (int64_t)q0 * k;
-    a.scores = scores + (int64_t)q0 * k;
+    const is::TopkLaunch a =
+        topk_launch_of(s, q, q0, nq, k, static_cast<char*>(sl->dev), lay, ids, scores);
     hipError_t e = is::launch_topk(a, st);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
     e = hipEventRecord(sl->done, st);
@@ -576,6 +606,7 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   is::clear_error();
   if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
   is_store* s = const_cast<is_store*>(cs);
+  std::lock_guard<std::mutex> lock(s->mu);   // n_facts, the index and the tables move under removals
   if (s->emb_dim == 0 || s->emb == nullptr)
     return fail(IS_ERR_UNSUPPORTED, "store has no embedding index");
   if (n_req < 0) return fail(IS_ERR_INVALID_ARG, "n_req < 0");
@@ -598,7 +629,6 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   const int32_t n_pairs = (int32_t)(g.size() / 2);
   if (n_pairs > is::kComposeMaxPairs) return fail(IS_ERR_UNSUPPORTED, "head_dim too large");
   DeviceGuard guard(s->device);
-  std::lock_guard<std::mutex> lock(s->mu);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // One scratch slot: top-k scratch (reused by each group of 128 queries),
   // then ids and scores of all requests, the work list, the rotation speeds
@@ -646,20 +676,8 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   int32_t* ids = ids_out ? ids_out : reinterpret_cast<int32_t*>(p + off_ids);
   float* scores = reinterpret_cast<float*>(p + off_scores);
   for (int32_t q0 = 0; q0 < n_req; q0 += 128) {
-    is::TopkLaunch a{};
-    a.emb = s->emb;
-    a.q = q + (int64_t)q0 * s->emb_dim;
-    a.n_facts = s->n_facts;
-    a.emb_dim = s->emb_dim;
-    a.n_q = std::min<int32_t>(128, n_req - q0);
-    a.k = k;
-    a.q_pad = reinterpret_cast<uint16_t*>(p + lay.q_off);
-    a.gmax = reinterpret_cast<uint32_t*>(p + lay.gmax_off);
-    a.tau = reinterpret_cast<float*>(p + lay.tau_off);
-    a.count = reinterpret_cast<uint32_t*>(p + lay.count_off);
-    a.cand = reinterpret_cast<uint64_t*>(p + lay.cand_off);
-    a.ids = ids + (int64_t)q0 * k;
-    a.scores = scores + (int64_t)q0 * k;
+    const is::TopkLaunch a =
+        topk_launch_of(s, q, q0, std::min<int32_t>(128, n_req - q0), k, p, lay, ids, scores);
     if ((e = is::launch_topk(a, st)) != hipSuccess) return hip_fail(e, "top-k launch");
   }
   is::ComposeLaunch c{};
@@ -850,6 +868,7 @@ IS_EXPORT int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, i
   if (s == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
   if (first_id == nullptr) return fail(IS_ERR_INVALID_ARG, "null first_id");
   if (n < 0 || window < 0) return fail(IS_ERR_INVALID_ARG, "n and window must be >= 0");
+  std::lock_guard<std::mutex> lock(s->mu);
   if (s->n_hbm < s->n_facts)
     return fail(IS_ERR_UNSUPPORTED, "appends need a store without a host tier");
   *first_id = s->n_facts;
@@ -868,7 +887,6 @@ IS_EXPORT int is_store_append(is_store* s, int32_t n, const int32_t* fact_len, i
       return fail(IS_ERR_INVALID_ARG, "a fact's layer must stay below 2^35 bytes");
   }
   DeviceGuard guard(s->device);
-  std::lock_guard<std::mutex> lock(s->mu);
   const int64_t f0 = s->n_facts;
   if (f0 + n > s->max_facts) return fail(IS_ERR_OOM, "no spare fact slots left in the store");
   // each new fact's block: first fit in the spans that removed facts left,
@@ -935,6 +953,7 @@ IS_EXPORT int is_store_update(is_store* s, int64_t fact_id, int32_t window, cons
                               const void* v_enc, const uint16_t* emb, void* stream) {
   is::clear_error();
   if (s == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  std::lock_guard<std::mutex> lock(s->mu);
   if (fact_id < 0 || fact_id >= s->n_facts) return fail(IS_ERR_FACT_ID, "fact id out of range");
   if (window < 0) return fail(IS_ERR_INVALID_ARG, "window must be >= 0");
   if (k_enc == nullptr || v_enc == nullptr) return fail(IS_ERR_INVALID_ARG, "null encoding");
@@ -943,8 +962,6 @@ IS_EXPORT int is_store_update(is_store* s, int64_t fact_id, int32_t window, cons
   if (emb != nullptr && s->emb_dim == 0)
     return fail(IS_ERR_INVALID_ARG, "store has no embedding index");
   DeviceGuard guard(s->device);
-  std::lock_guard<std::mutex> lock(s->mu);
-  if (fact_id >= s->n_facts) return fail(IS_ERR_FACT_ID, "fact id out of range");
   const int32_t len = s->len[(size_t)fact_id];
   if ((int64_t)window + len > ((int64_t)1 << 24))
     return fail(IS_ERR_INVALID_ARG, "window + fact length must stay below 2^24");

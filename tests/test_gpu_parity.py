@@ -136,6 +136,39 @@ def test_inject_deterministic_and_position_zero_identity(gpu):
         st.destroy()
 
 
+@pytest.mark.parametrize("dtype,head_dim", [(synth.F32, 64), (synth.F32, 128), (synth.F32, 32),
+                                            (synth.BF16, 128), (synth.BF16, 64)])
+def test_position_zero_identity_bit_exact(gpu, dtype, head_dim):
+    """A key injected at position 0 turns by angle 0: the cache row equals the
+    stored pre-RoPE row bit for bit, for every layer and head, in both cache
+    dtypes and in both inject kernels (256-byte rows: fp32 d64, bf16 d128;
+    other rows: fp32 d128 and d32, bf16 d64)."""
+    w = SMALL_LLAMA.scaled(name=f"p0_{dtype}_{head_dim}", n_layers=3, n_kv_heads=4,
+                           head_dim=head_dim, dtype=dtype, n_facts=60, n_blocks=200,
+                           theta=1e6, scaling="none")
+    lens, req_off, flat, _, _ = _zipf_problem(w, 5, 4)
+    prefix = np.zeros(5, np.int32)
+    bt = Hn.block_tables_for(w, lens, req_off, flat, prefix)
+    st = Hn.make_store(w, lens)
+    try:
+        cache = Hn.make_cache(w)
+        Hn.gpu_inject(st, cache, req_off, flat, prefix, bt)
+        import torch
+        torch.cuda.synchronize()
+        es = w.elem_size
+        view = cache.k.view(w.n_layers, w.n_blocks, w.block_size, w.n_kv_heads,
+                            w.head_dim * es)
+        for r in range(5):
+            f = int(flat[req_off[r]])
+            k_pre = synth.fact_kv(w.seed, synth.TAG_K, f, int(lens[f]) * w.row_elems, w.dtype)
+            k_pre = k_pre.reshape(w.n_layers, w.n_kv_heads, int(lens[f]), w.head_dim)[:, :, 0]
+            got = view[:, int(bt[r, 0]), 0].cpu().numpy()
+            want = np.ascontiguousarray(k_pre).view(np.uint8)
+            assert np.array_equal(got.reshape(want.shape), want), f"request {r}"
+    finally:
+        st.destroy()
+
+
 def test_inject_invalid_call_writes_nothing(gpu):
     import torch
     w = SMALL_LLAMA

@@ -18,6 +18,11 @@ MUTANTS = {
     "freq_index": ("pow(theta, -2.0 * i / d)", "pow(theta, -2.0 * (i + 1) / d)"),
     "llama3_blend": ("(1.0 - smooth) * f / factor + smooth * f",
                      "smooth * f / factor + (1.0 - smooth) * f"),
+    # a blend that is linear in the wavelength: same values at both band edges,
+    # monotone, strictly inside (f/8, f), but not the published rule inside
+    "llama3_blend_in_wavelength": ("const double smooth = (orig / wavelen - low) / (high - low);",
+                                   "const double smooth = (orig / low - wavelen) / "
+                                   "(orig / low - orig / high);"),
     "bf16_ties_away": ("nearbyint(x / quantum) * quantum", "floor(x / quantum + 0.5) * quantum"),
     "topk_tie_order": ("return (x->id > y->id) - (x->id < y->id);",
                        "return (x->id < y->id) - (x->id > y->id);"),

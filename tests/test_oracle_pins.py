@@ -115,6 +115,39 @@ def test_llama3_scaling_bands():
     assert np.all(np.diff(g) < 0)
 
 
+def test_llama3_scaling_interior_closed_form():
+    """Inside the blended band the published Llama-3.1 rule moves the
+    multiplier f'/f from 1/factor to 1 in proportion to how far orig/lambda
+    has moved from `low` to `high`.  At lambda = 4096, orig/lambda = 2, one
+    third of the way from 1 to 4: f' = (2/3)(f/8) + (1/3)f = 5f/12.  At
+    lambda = 3072, orig/lambda = 8/3, five ninths of the way:
+    f' = (4/9)(f/8) + (5/9)f = 11f/18.  At lambda = 6553.6, orig/lambda =
+    1.25, one twelfth: f' = (11/12)(f/8) + f/12 = 19f/96."""
+    for lam, ratio in ((4096.0, 5 / 12), (3072.0, 11 / 18), (6553.6, 19 / 96)):
+        f = 2 * math.pi / lam
+        assert oracle.llama3_scale(f) == pytest.approx(ratio * f, rel=1e-13)
+    # other parameters: factor 4, low 2, high 8, orig 16384; lambda = 4096 gives
+    # orig/lambda = 4, one third of the way from 2 to 8: f' = (2/3)(f/4) + f/3 = f/2
+    f = 2 * math.pi / 4096.0
+    assert oracle.llama3_scale(f, 4.0, 2.0, 8.0, 16384.0) == pytest.approx(f / 2, rel=1e-13)
+
+
+def test_llama3_scaling_multiplier_affine_in_frequency():
+    """orig/lambda = orig f / 2pi is proportional to f, so across the band the
+    multiplier f'/f is an affine function of f itself: 1/8 at the band's
+    low-frequency edge (lambda = 8192) and 1 at its high-frequency edge
+    (lambda = 2048).  Checked on the six blended frequencies of d = 128,
+    theta = 5e5 and on a dense sweep of the band."""
+    f_lo, f_hi = 2 * math.pi / 8192.0, 2 * math.pi / 2048.0
+    f = oracle.rope_freqs(128, 500000.0)
+    lam = 2 * np.pi / f
+    band = f[(lam >= 2048) & (lam <= 8192)]
+    sweep = np.linspace(f_lo, f_hi, 101)[1:-1]
+    for ff in list(band) + list(sweep):
+        m = oracle.llama3_scale(float(ff)) / ff
+        assert m == pytest.approx(1 / 8 + (7 / 8) * (ff - f_lo) / (f_hi - f_lo), rel=1e-12)
+
+
 def test_llama3_scaling_continuous_at_band_edges():
     for lam_edge, expect in ((2048.0, 1.0), (8192.0, 1 / 8.0)):
         f = 2 * np.pi / lam_edge
