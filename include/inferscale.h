@@ -203,6 +203,22 @@ int is_topk(const is_store* s, const uint16_t* q_f16, int32_t n_q, int32_t k,
             int32_t* ids, float* scores, void* stream);
 
 /*
+ * is_topk for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results (bit for bit) and errors as is_topk, but the
+ * call allocates nothing: its scratch is one fixed 72 MiB array in device
+ * memory per GPU, held from the first call on that GPU until the process
+ * ends, instead of the store's scratch ring.  Limit: stores of at most
+ * 65,536 facts (larger stores: IS_ERR_UNSUPPORTED, nothing enqueued).
+ * Every call on one GPU uses the same array, whatever its store, so calls
+ * that overlap on a GPU (other streams, other host threads) race: order
+ * them.  No part of the array needs clearing between calls (each call
+ * writes every element it reads before reading it).
+ */
+int is_topk_noalloc(const is_store* s, const uint16_t* q_f16, int32_t n_q, int32_t k,
+                    int32_t* ids, float* scores, void* stream);
+
+/*
  * (Online phase: the retrieved facts are composed into one contiguous
  * segment, every stored key gets the RoPE rotation of its new serving
  * position -- dynamic rotation, exact by Theorem 6 -- and the K/V are

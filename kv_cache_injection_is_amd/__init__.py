@@ -24,7 +24,8 @@ STATUS = {0: "IS_OK", -1: "IS_ERR_INVALID_ARG", -2: "IS_ERR_FACT_ID", -3: "IS_ER
 IS_DTYPE_F32, IS_DTYPE_BF16 = 0, 1
 IS_ROPE_NONE, IS_ROPE_LLAMA3 = 0, 1
 
-EXPORTS = ("is_store_create", "is_store_load", "is_store_get_info", "is_topk", "is_inject",
+EXPORTS = ("is_store_create", "is_store_load", "is_store_get_info", "is_topk",
+           "is_topk_noalloc", "is_inject",
            "is_retrieve_inject", "is_attend", "is_store_append", "is_store_update",
            "is_store_remove", "is_inject_check", "is_store_destroy", "is_last_error")
 
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.is_store_load.argtypes = [P, c.c_int64, c.c_int64, P, P, P, c.c_int]
         L.is_store_get_info.argtypes = [P, c.POINTER(is_store_info)]
         L.is_topk.argtypes = [P, P, c.c_int32, c.c_int32, P, P, P]
+        L.is_topk_noalloc.argtypes = [P, P, c.c_int32, c.c_int32, P, P, P]
         L.is_inject.argtypes = [P, c.c_int32, P, P, P, P, c.c_int32, c.POINTER(is_cache),
                                 c.POINTER(is_rope), P]
         L.is_retrieve_inject.argtypes = [P, P, c.c_int32, c.c_int32, P, P, c.c_int32,
@@ -182,6 +184,12 @@ def is_store_get_info(store: int) -> is_store_info:
 def is_topk(store: int, q_f16, n_q: int, k: int, ids, scores, stream=None) -> None:
     """q_f16, ids, scores: device tensors (int16/uint16-viewed fp16, int32, float32)."""
     _check(lib().is_topk(store, _dev(q_f16), n_q, k, _dev(ids), _dev(scores), _stream(stream)))
+
+
+def is_topk_noalloc(store: int, q_f16, n_q: int, k: int, ids, scores, stream=None) -> None:
+    """As is_topk, with the library's fixed per-GPU scratch (no allocation)."""
+    _check(lib().is_topk_noalloc(store, _dev(q_f16), n_q, k, _dev(ids), _dev(scores),
+                                 _stream(stream)))
 
 
 def is_retrieve_inject(store: int, q_f16, n_req: int, k: int, prefix_len, block_tables,

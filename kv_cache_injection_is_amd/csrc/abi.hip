@@ -599,6 +599,71 @@ IS_EXPORT int is_topk(const is_store* cs, const uint16_t* q, int32_t n_q, int32_
   return IS_OK;
 }
 
+// Scratch of is_topk_noalloc: a fixed array in device memory, one copy per
+// GPU, held until the process ends.  Host code never uses the array's name
+// as an address (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current.  Its size holds the largest scratch that the accepted
+// stores need: 128 queries x 65,536 facts of 8-byte candidate keys (64 MiB),
+// padded queries of the widest index (4 MiB) and the sample maxima, bounds
+// and counts.
+constexpr int64_t kNoAllocMaxFacts = 65536;
+constexpr size_t kNoAllocScratchBytes = size_t(72) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev` (which must be current).
+int scratch_on_device(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(IS_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return IS_OK;
+}
+
+}  // namespace
+
+IS_EXPORT int is_topk_noalloc(const is_store* cs, const uint16_t* q, int32_t n_q, int32_t k,
+                              int32_t* ids, float* scores, void* stream) {
+  is::clear_error();
+  if (cs == nullptr) return fail(IS_ERR_INVALID_ARG, "null store");
+  is_store* s = const_cast<is_store*>(cs);
+  std::lock_guard<std::mutex> lock(s->mu);
+  bool nothing = false;
+  int rc = check_topk_call(s, q, n_q, k, ids, scores, &nothing);
+  if (rc != IS_OK || nothing) return rc;
+  if (s->n_facts > kNoAllocMaxFacts)
+    return fail(IS_ERR_UNSUPPORTED,
+                "is_topk_noalloc covers stores of at most 65,536 facts (its fixed scratch is "
+                "72 MiB per GPU); use is_topk");
+  const is::TopkScratch lay = is::topk_scratch(s->n_facts, std::min<int32_t>(128, n_q), s->emb_dim);
+  if (lay.bytes > kNoAllocScratchBytes)
+    return fail(IS_ERR_UNSUPPORTED, "the call's scratch exceeds the fixed 72 MiB");
+  DeviceGuard guard(s->device);
+  char* p = nullptr;
+  rc = scratch_on_device(s->device, &p);
+  if (rc != IS_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // groups of 128 queries reuse the scratch one after the other on `stream`
+  for (int32_t q0 = 0; q0 < n_q; q0 += 128) {
+    const int32_t nq = std::min<int32_t>(128, n_q - q0);
+    const is::TopkScratch lg = is::topk_scratch(s->n_facts, nq, s->emb_dim);
+    const hipError_t e = is::launch_topk(topk_launch_of(s, q, q0, nq, k, p, lg, ids, scores), st);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  }
+  return IS_OK;
+}
+
 IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t n_req, int32_t k,
                                  const int32_t* prefix_len, const int32_t* block_tables,
                                  int32_t max_blocks, const is_cache* cache, const is_rope* rope,

@@ -32,6 +32,7 @@ def test_null_arguments_are_rejected_without_gpu():
     assert "null" in K.is_last_error()
     assert lib.is_store_destroy(None) == 0
     assert lib.is_topk(None, None, 1, 1, None, None, None) == -1
+    assert lib.is_topk_noalloc(None, None, 1, 1, None, None, None) == -1
     assert lib.is_inject(None, 0, None, None, None, None, 1, None, None, None) == -1
     assert lib.is_retrieve_inject(None, None, 1, 1, None, None, 1, None, None, None, None,
                                   None) == -1
