@@ -241,13 +241,41 @@ def k_tolerance(ref: np.ndarray, dtype: int) -> np.ndarray:
     return np.maximum(ulp, 2.0 ** -15)
 
 
+def generator_blocks(w: W.Workload, lens, facts, tag: int) -> np.ndarray:
+    """K (tag 1) or V (tag 2) blocks of `facts`, back to back, made by the
+    generator's device build (bit-equal to its host build; the host build is
+    slower at full size) and copied to the host.  The generator is the input
+    module both sides share; no part of the library is involved."""
+    torch = torch_mod()
+    facts = np.asarray(facts, dtype=np.int64)
+    row = w.row_elems
+    n = lens[facts].astype(np.int64) * row
+    off = np.zeros(len(facts) + 1, dtype=np.int64)
+    np.cumsum(n, out=off[1:])
+    out = torch.empty(max(int(off[-1]), 1) * w.elem_size, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    i = 0
+    while i < len(facts):
+        j = i + 1                      # a run of consecutive fact ids: one fill
+        while j < len(facts) and facts[j] == facts[j - 1] + 1:
+            j += 1
+        d_off = torch.from_numpy(off[i:j + 1] - off[i]).cuda()
+        synth.gpu_fill_kv(w.seed, tag, int(facts[i]), d_off, int(off[j] - off[i]), w.dtype,
+                          out.data_ptr() + int(off[i]) * w.elem_size, st)
+        i = j
+    torch.cuda.synchronize()
+    return out[:int(off[-1]) * w.elem_size].cpu().numpy().view(synth.kv_dtype_np(w.dtype))
+
+
 def oracle_blocks(w: W.Workload, lens, req_off, flat_ids, prefix, bt, blocks, layout,
-                  cache_nb, rows=None):
+                  cache_nb, rows=None, touched_only=False):
     """Runs the oracle on the given requests into a compact host cache that
     holds only `blocks` (physical ids, remapped to 0..m-1), initialised to
-    the same sentinel the GPU cache was filled with.  Returns (k, v) arrays
-    [L][m][B*H*d] in the cache's layout, raw bytes.  `rows` maps a fact id
-    to its (K, V) store blocks where they are not the generator's."""
+    the same sentinel the GPU cache was filled with (to zeros when only the
+    touched rows will be compared; the K/V inputs then come from the
+    generator's device build).  Returns (k, v) arrays [L][m][B*H*d] in the
+    cache's layout, raw bytes.  `rows` maps a fact id to its (K, V) store
+    blocks where they are not the generator's."""
     L, H, d, B, es = w.n_layers, w.n_kv_heads, w.head_dim, w.block_size, w.elem_size
     uniq = np.unique(flat_ids)
     remap = {int(f): i for i, f in enumerate(uniq)}
@@ -262,20 +290,28 @@ def oracle_blocks(w: W.Workload, lens, req_off, flat_ids, prefix, bt, blocks, la
         if int(f) in rows:
             return rows[int(f)][i]
         return synth.fact_kv(w.seed, tag, int(f), int(lens[f]) * row, w.dtype)
-    Kh = np.concatenate([block(f, synth.TAG_K, 0) for f in uniq] or empty)
-    Vh = np.concatenate([block(f, synth.TAG_V, 1) for f in uniq] or empty)
+    if touched_only and not rows and len(uniq):
+        Kh = generator_blocks(w, lens, uniq, synth.TAG_K)
+        Vh = generator_blocks(w, lens, uniq, synth.TAG_V)
+    else:
+        Kh = np.concatenate([block(f, synth.TAG_K, 0) for f in uniq] or empty)
+        Vh = np.concatenate([block(f, synth.TAG_V, 1) for f in uniq] or empty)
     blocks = np.asarray(blocks, dtype=np.int64)
     bmap = {int(b): i for i, b in enumerate(blocks)}
     bt_c = np.vectorize(lambda b: bmap.get(int(b), -1))(bt).astype(np.int32)
     m = len(blocks)
     blk_words = B * H * d * es // 4
-    kc = np.empty((L, m, blk_words), dtype=np.uint32)
-    vc = np.empty((L, m, blk_words), dtype=np.uint32)
-    for l in range(L):
-        for i, b in enumerate(blocks):
-            first = (l * cache_nb + int(b)) * blk_words
-            kc[l, i] = synth.sentinel_host(SENTINEL_SEED_K, first, blk_words)
-            vc[l, i] = synth.sentinel_host(SENTINEL_SEED_V, first, blk_words)
+    if touched_only:
+        kc = np.zeros((L, m, blk_words), dtype=np.uint32)
+        vc = np.zeros((L, m, blk_words), dtype=np.uint32)
+    else:
+        kc = np.empty((L, m, blk_words), dtype=np.uint32)
+        vc = np.empty((L, m, blk_words), dtype=np.uint32)
+        for l in range(L):
+            for i, b in enumerate(blocks):
+                first = (l * cache_nb + int(b)) * blk_words
+                kc[l, i] = synth.sentinel_host(SENTINEL_SEED_K, first, blk_words)
+                vc[l, i] = synth.sentinel_host(SENTINEL_SEED_V, first, blk_words)
     if layout == "NHD":
         strides = (m * B * H * d, B * H * d, H * d, d)
     else:
@@ -319,28 +355,36 @@ def gpu_blocks(cache: Cache, blocks):
     return (kk.index_select(1, idx).cpu().numpy(), vv.index_select(1, idx).cpu().numpy())
 
 
-def check_inject_blocks(cache: Cache, lens, req_off, flat_ids, prefix, bt, blocks, rows=None):
+def check_inject_blocks(cache: Cache, lens, req_off, flat_ids, prefix, bt, blocks, rows=None,
+                        touched_only=False):
     """Element-by-element comparison of the GPU cache and the oracle on the
     given physical blocks (all layers).  Returns (#elements compared, max K
-    error).  `rows`: as for oracle_blocks."""
+    error).  `rows`: as for oracle_blocks.  With touched_only the comparison
+    covers the rows the requests write (V bit-exact, K within tolerance) and
+    leaves the untouched rows to check_untouched, which covers the whole
+    cache on the device."""
     w = cache.w
     es = w.elem_size
     kc_o, vc_o = oracle_blocks(w, lens, req_off, flat_ids, prefix, bt, blocks, cache.layout,
-                               cache.n_blocks, rows)
+                               cache.n_blocks, rows, touched_only)
     kg, vg = gpu_blocks(cache, blocks)
     mask_e, _ = touched_mask(w, lens, req_off, flat_ids, prefix, bt, blocks, cache.layout)
     L, m = w.n_layers, len(blocks)
     ko = kc_o.view(np.uint8).reshape(L, m, -1)
     vo = vc_o.view(np.uint8).reshape(L, m, -1)
-    # V and every untouched byte: bit-exact
-    assert np.array_equal(vg, vo), "V cache differs from the oracle"
     mask_b = np.repeat(mask_e, es, axis=1)
-    for l in range(L):
-        assert np.array_equal(kg[l][~mask_b], ko[l][~mask_b]), f"untouched K bytes changed (layer {l})"
-    ref = _as_f64(ko, w.dtype)
-    got = _as_f64(kg, w.dtype)
-    ref = ref.reshape(L, m, -1)[:, mask_e]
-    got = got.reshape(L, m, -1)[:, mask_e]
+    if touched_only:
+        for l in range(L):
+            assert np.array_equal(vg[l][mask_b], vo[l][mask_b]), f"V differs (layer {l})"
+    else:
+        # V and every untouched byte: bit-exact
+        assert np.array_equal(vg, vo), "V cache differs from the oracle"
+        for l in range(L):
+            assert np.array_equal(kg[l][~mask_b], ko[l][~mask_b]), \
+                f"untouched K bytes changed (layer {l})"
+    ew = 4 if w.dtype == synth.F32 else 2
+    ref = _as_f64(np.ascontiguousarray(ko).view(f"u{ew}").reshape(L, m, -1)[:, mask_e], w.dtype)
+    got = _as_f64(np.ascontiguousarray(kg).view(f"u{ew}").reshape(L, m, -1)[:, mask_e], w.dtype)
     tol = k_tolerance(ref, w.dtype)
     err = np.abs(got - ref)
     bad = err > tol
