@@ -2,14 +2,17 @@
 
 One step = one batch of the whole path on the Mistral-7B-shaped workload
 (32 layers x 8 kv_heads x head_dim 128, bf16, 50,000 facts with lognormal
-lengths, fp16 embeddings 50,000 x 1024): exact top-50 for 100 queries
-(is_topk), the ids back to the host, then composition, validation, gather,
-Chunked-RoPE re-rotation and paged scatter of all 100 x 50 selected facts
-(is_inject).  Inputs are synthetic (seeded generator) and resident in HBM
-before the timed region.
+lengths, fp16 embeddings 50,000 x 1024): exact top-50 for 100 queries, then
+composition, validation, gather, Chunked-RoPE re-rotation and paged scatter
+of all 100 x 50 selected facts, all on the device (is_retrieve_inject: the
+ids never visit the host).  The same batch through the host path (is_topk,
+the ids to the host, is_inject) is timed the same way and reported beside
+it.  Inputs are synthetic (seeded generator) and resident in HBM before the
+timed region.
 
-Prints one JSON line: injected tokens/s for the whole step, plus the
-inject kernel's roofline (algorithmic bytes / HIP-event kernel time against
+Prints one JSON line: injected tokens/s for the whole step and the step's
+fraction of 8 TB/s (top-k + inject algorithmic bytes per step), the inject
+kernel's roofline (algorithmic bytes / HIP-event kernel time against
 8 TB/s), the top-k rate (back to back, and with the caches flushed before
 each call), the top-k rate over the Qwen-shaped 1M x 1024 embeddings, and
 the fp64 CPU oracle timed on a bounded sample of the same workload.
@@ -705,7 +708,19 @@ def main() -> int:
     tokens = int(st.lens[flat0].sum())
     log(f"cache ready: {cache.n_blocks} blocks; {tokens} injected tokens per step")
 
+    # The step: is_retrieve_inject (top-k, composition, validation, inject on
+    # the device).  Its prefixes, block tables and status word live in HBM.
+    status = torch.full((1,), 1, dtype=torch.int32, device="cuda")
+    d_prefix = torch.from_numpy(np.ascontiguousarray(prefix, np.int32)).cuda()
+    d_bt = torch.from_numpy(np.ascontiguousarray(bt, np.int32)).cuda()
+    ids_step = torch.full((n_q, k), -1, dtype=torch.int32, device="cuda")
+
     def step():
+        K.is_retrieve_inject(st.handle, q, n_q, k, d_prefix, d_bt, cdesc, rope, status, ids_step,
+                             stream)
+
+    # The host path of the same batch: top-k, ids to the host, inject.
+    def host_step():
         K.is_topk(st.handle, q, n_q, k, ids_d, sc_d, stream)
         ids_h.copy_(ids_d, non_blocking=True)
         stream.synchronize()
@@ -713,23 +728,32 @@ def main() -> int:
         K.is_inject(st.handle, req_off, flat, prefix, bt, cdesc, rope, stream)
         return flat
 
+    def timed_steps(fn, n):
+        """Wall time of n back-to-back steps between two synchronizes, and
+        the per-step launch-to-launch intervals."""
+        torch.cuda.synchronize()
+        marks = []
+        t0 = time.perf_counter()
+        for _ in range(n):
+            marks.append(time.perf_counter())
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        marks.append(t1)
+        return (t1 - t0) * 1e3 / n, np.diff(np.array(marks)) * 1e3
+
     for _ in range(args.warmup):
         step()
+        host_step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    marks = []
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        marks.append(time.perf_counter())
-        flat = step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    marks.append(t1)
+    log(f"timing {args.steps} steps (device path), then {args.steps} host-path steps")
+    ms_step, step_ms = timed_steps(step, args.steps)
+    assert int(status.item()) == 0, "device-side validation failed"
+    assert np.array_equal(ids_step.cpu().numpy().reshape(-1), flat0), \
+        "retrieval changed between steps"
+    host_ms_step, host_step_ms = timed_steps(host_step, args.steps)
+    flat = ids_h.numpy().reshape(-1)
     assert np.array_equal(flat, flat0), "retrieval changed between steps"
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    # step i's interval runs from its start to the next step's start (each
-    # step waits for the previous inject when it synchronizes on its ids)
-    step_ms = np.diff(np.array(marks)) * 1e3
 
     # Per-kernel times: the same calls launched back to back on the same
     # stream, bracketed by HIP events (host planning overlaps the previous
@@ -759,7 +783,9 @@ def main() -> int:
     topk_bytes = w.n_facts * w.emb_dim * 2 + n_q * w.emb_dim * 2 + n_q * k * 8
     topk_gbps = topk_bytes / (topk_ms / 1e3) / 1e9
     value = tokens / (ms_step / 1e3)
-    log(f"step {ms_step:.3f} ms; inject {inject_ms:.3f} ms ({inj_gbps:.0f} GB/s); "
+    step_frac = (inj_bytes + topk_bytes) / (ms_step / 1e3) / (HBM_PEAK_GBPS * 1e9)
+    log(f"step {ms_step:.3f} ms (fraction of 8 TB/s {step_frac:.3f}; host path "
+        f"{host_ms_step:.3f} ms); inject {inject_ms:.3f} ms ({inj_gbps:.0f} GB/s); "
         f"top-k {topk_ms:.3f} ms")
 
     dev = device_path(torch, K, st, w, q, stream, cdesc, rope, prefix, bt, tokens,
@@ -837,6 +863,16 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, p)), 4) for p in (10, 50, 90)],
+        "step_frac": round(step_frac, 4),
+        "step_frac_note": "(top-k + inject algorithmic bytes per step) / ms_per_step / 8 TB/s",
+        "step_bytes": inj_bytes + topk_bytes,
+        "host_path": {
+            "ms_per_step": round(host_ms_step, 4),
+            "tokens_per_s": round(tokens / (host_ms_step / 1e3), 1),
+            "step_frac": round((inj_bytes + topk_bytes) / (host_ms_step / 1e3) /
+                               (HBM_PEAK_GBPS * 1e9), 4),
+            "note": "is_topk, the ids to the host (pinned), is_inject: the same batch with "
+                    "host-side composition and validation"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

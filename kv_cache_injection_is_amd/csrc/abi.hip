@@ -465,21 +465,28 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
                            max_blocks, cache, rope, &items, &n_tokens);
   if (rc != IS_OK) return rc;
   if (items.empty()) return IS_OK;
-  // Launch order only: by fact id (stable), which is the store's layout
-  // order (HBM facts, then the host tier, each in id order), so the
-  // workgroups sweep the store front to back.  LSD radix sort, 11-bit digits.
+  // Launch order only: host-tier facts first, then HBM facts, each tier by
+  // fact id (stable), which is the store's layout order, so the workgroups
+  // sweep each tier front to back, and the PCIe-bound host-tier reads start
+  // at once with the HBM work filling in behind them.  LSD radix sort of the
+  // rotated id (id - n_hbm modulo n_facts), 11-bit digits.
   thread_local std::vector<uint32_t> order, spare;
   const uint32_t n_items = (uint32_t)items.size();
   order.resize(n_items);
   spare.resize(n_items);
   for (uint32_t i = 0; i < n_items; ++i) order[i] = i;
   const uint32_t max_id = (uint32_t)(s->n_facts - 1);
+  const uint32_t n_hbm = (uint32_t)s->n_hbm, n_host = (uint32_t)(s->n_facts - s->n_hbm);
+  auto key = [&](uint32_t i) {
+    const uint32_t f = (uint32_t)fact_ids[i];
+    return f >= n_hbm ? f - n_hbm : f + n_host;
+  };
   for (int shift = 0; shift == 0 || (shift < 32 && (max_id >> shift) != 0); shift += 11) {
     uint32_t hist[2049] = {};
-    for (uint32_t i = 0; i < n_items; ++i) ++hist[(((uint32_t)fact_ids[order[i]] >> shift) & 2047u) + 1];
+    for (uint32_t i = 0; i < n_items; ++i) ++hist[((key(order[i]) >> shift) & 2047u) + 1];
     for (int b = 0; b < 2048; ++b) hist[b + 1] += hist[b];
     for (uint32_t i = 0; i < n_items; ++i)
-      spare[hist[((uint32_t)fact_ids[order[i]] >> shift) & 2047u]++] = order[i];
+      spare[hist[(key(order[i]) >> shift) & 2047u]++] = order[i];
     order.swap(spare);
   }
   is::plan_rope(s->d, rope, &g);
@@ -518,6 +525,7 @@ IS_EXPORT int is_inject(const is_store* cs, int32_t n_req, const int32_t* req_of
   a.head_dim = s->d;
   a.dtype = s->dtype;
   a.lanes = is::inject_lanes(s->d, s->dtype);
+  a.mean_len = (float)n_tokens / (float)n_items;
   e = is::launch_inject(a, st);
   if (e != hipSuccess) return hip_fail(e, "inject launch");
   e = hipEventRecord(sl->done, st);
@@ -788,6 +796,8 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   a.dtype = s->dtype;
   a.lanes = is::inject_lanes(s->d, s->dtype);
   a.status = status;
+  // the ids are chosen on the device: the store's mean fact length stands in
+  a.mean_len = (float)s->tok_off[(size_t)s->n_facts] / (float)s->n_facts;
   if ((e = is::launch_inject(a, st)) != hipSuccess) return hip_fail(e, "inject launch");
   if (!capturing && (e = hipEventRecord(sl->done, st)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");

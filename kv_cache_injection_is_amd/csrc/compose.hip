@@ -17,7 +17,8 @@
 // the bitmap with 64-bit atomic ORs -- a bit that was already set is a slot
 // used twice; and, for batches, a counting sort of the list into 4096
 // consecutive fact-id ranges (launch order only: the inject grid then walks
-// the store front to back, as the host path's sorted list does; the order
+// the host tier and then HBM front to back, as the host path's sorted list
+// does; the order
 // inside a range is whatever the atomics give, which changes no result,
 // since every item writes its own slots).
 #include <hip/hip_runtime.h>
@@ -41,8 +42,12 @@ __global__ __launch_bounds__(kClearThreads) void compose_clear(ComposeLaunch a) 
 
 __device__ __forceinline__ void record(int32_t* status, int32_t code) { atomicMin(status, code); }
 
-__device__ __forceinline__ int bucket_of(int32_t f, int64_t n_facts) {
-  return (int)((int64_t)f * kComposeBuckets / n_facts);
+// Launch-order bucket of fact f: host-tier facts (ids from n_hbm on) first,
+// so the PCIe-bound part of the batch starts at once and the HBM facts fill
+// in behind it; each tier in id order.
+__device__ __forceinline__ int bucket_of(int32_t f, int64_t n_facts, int64_t n_hbm) {
+  const int64_t rot = (int64_t)f >= n_hbm ? (int64_t)f - n_hbm : (int64_t)f + (n_facts - n_hbm);
+  return (int)(rot * kComposeBuckets / n_facts);
 }
 
 // Sets bits [b0, b1] of the bitmap; true if one of them was set already.
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(64) void compose(ComposeLaunch a) {
   const int32_t f = mine ? a.ids[(int64_t)r * a.k + lane] : 0;
   const bool id_ok = f >= 0 && (int64_t)f < a.n_facts;
   if (mine && !id_ok) record(a.status, IS_ERR_FACT_ID);
-  if (mine && id_ok && a.work_tmp != nullptr) atomicAdd(&a.buckets[bucket_of(f, a.n_facts)], 1u);
+  if (mine && id_ok && a.work_tmp != nullptr) atomicAdd(&a.buckets[bucket_of(f, a.n_facts, a.n_hbm)], 1u);
   const int64_t len = (mine && id_ok) ? a.lens[f] : 0;
   // inclusive scan of the lengths across the wave
   int64_t incl = len;
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(256) void bucket_scatter(ComposeLaunch a) {
   if (i >= (int64_t)a.n_req * a.k) return;
   const int32_t f = a.ids[i];
   if (f < 0 || (int64_t)f >= a.n_facts) return;
-  const uint32_t slot = atomicAdd(&a.buckets[kComposeBuckets + bucket_of(f, a.n_facts)], 1u);
+  const uint32_t slot = atomicAdd(&a.buckets[kComposeBuckets + bucket_of(f, a.n_facts, a.n_hbm)], 1u);
   a.work[slot] = a.work_tmp[i];
 }
 

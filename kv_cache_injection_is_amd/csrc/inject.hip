@@ -49,19 +49,31 @@
 #define IS_R16 1                // use it where it applies
 #endif
 #ifndef IS_R16_THREADS
-#define IS_R16_THREADS 512
-#endif
-#ifndef IS_R16_LAYERS
-#define IS_R16_LAYERS 1         // layers per workgroup
+#define IS_R16_THREADS 512      // lanes per workgroup for long facts
 #endif
 #ifndef IS_R16_ROWS
-#define IS_R16_ROWS 8           // rows in flight per lane
+#define IS_R16_ROWS 8           // rows in flight per lane, long facts
+#endif
+#ifndef IS_R16_SHORT_ROWS
+#define IS_R16_SHORT_ROWS 128   // below this many rows per layer (kv_heads x mean fact length)
+#endif                          // a workgroup takes several layers, with 256 lanes
+#ifndef IS_R16_SHORT_THREADS
+#define IS_R16_SHORT_THREADS 256  // lanes per workgroup for short facts
+#endif
+#ifndef IS_R16_SHORT_U
+#define IS_R16_SHORT_U 4        // rows in flight per lane, short facts
+#endif
+#ifndef IS_R16_FIXED_LAYERS
+#define IS_R16_FIXED_LAYERS 0   // > 0: that many layers per workgroup, whatever the lengths
 #endif
 #ifndef IS_R16_TC
 #define IS_R16_TC 64            // tokens per cos/sin pass
 #endif
 #ifndef IS_R16_LAYER_FAST
 #define IS_R16_LAYER_FAST 1     // grid x = layer group (consecutive workgroups share a fact)
+#endif
+#ifndef IS_R16_HOST_WHOLE
+#define IS_R16_HOST_WHOLE 1     // one workgroup moves all layers of a host-tier fact
 #endif
 
 namespace is {
@@ -223,9 +235,15 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectLaunch a) {
 // 16-byte chunk each, so a wave's load or store covers four whole rows.  The
 // rotate-half partner of lane c (first half) is lane c + 8 (second half) of
 // the same 16-lane row; the pair swap is a DPP rotate by 8 within the row.
-// A workgroup handles G consecutive layers of one selected fact: those
-// layers' [kv_head][token][head_dim] blocks are one contiguous span.
-template <int ES, int T, int G, int U, int TC>
+// A workgroup handles G consecutive layers of one selected fact (G set per
+// launch): those layers' [kv_head][token][head_dim] blocks are one
+// contiguous span.  A workgroup's start (work item, cos/sin, slot offsets,
+// barrier, then the first loads) costs about 2 us whatever it moves, so
+// short facts take several layers per workgroup: with one layer each, a
+// batch of 1-3 token facts is bound by workgroup starts, not by memory.  A
+// fact of the host tier is moved by one workgroup, all its layers (one span
+// of pinned memory); the other workgroups of its grid row exit at once.
+template <int ES, int T, int U, int TC>
 __global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
   constexpr int VEC = 16 / ES;      // elements per lane
   constexpr int HALF = 8 * VEC;     // head_dim / 2
@@ -237,17 +255,18 @@ __global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
   if (a.status != nullptr && *a.status != 0) return;   // the call failed validation
 #if IS_R16_LAYER_FAST
   const WorkItem w = a.work[blockIdx.y];
-  const int l0 = blockIdx.x * G;
+  const int grp = blockIdx.x;
 #else
   const WorkItem w = a.work[blockIdx.x];
-  const int l0 = blockIdx.y * G;
+  const int grp = blockIdx.y;
 #endif
-  const int nl = min(G, a.n_layers - l0);
+  const int G = a.layers_per_wg;
+  const bool whole = IS_R16_HOST_WHOLE && w.tier != 0;
+  if (whole && grp != 0) return;
+  const int l_begin = whole ? 0 : grp * G;
+  const int l_end = whole ? a.n_layers : min(a.n_layers, l_begin + G);
   const int len = w.len;
   const int H = a.n_heads;
-  const int64_t base = (int64_t)l0 * H * len * D * ES;
-  const char* __restrict__ ksrc = reinterpret_cast<const char*>(w.k) + base;
-  const char* __restrict__ vsrc = reinterpret_cast<const char*>(w.v) + base;
   char* __restrict__ kc = static_cast<char*>(a.kc);
   char* __restrict__ vc = static_cast<char*>(a.vc);
   const int32_t* __restrict__ bt = a.bt + (int64_t)w.req * a.max_blocks;
@@ -272,62 +291,70 @@ __global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
     }
     __syncthreads();
     const int per_layer = H * tc;
-    const int rows = nl * per_layer;
     const float inv_pl = 1.0f / (float)per_layer;
     const float inv_tc = 1.0f / (float)tc;
-    for (int r0 = tid / 16; r0 < rows; r0 += U * RPS) {
-      u32x4 kv[U], vv[U];
-      int gl[U], hh[U], tt[U];
+    // layers per pass: a pass indexes its rows below 2^16, where the row
+    // decomposition by float reciprocals is exact
+    const int lpp = max(1, 65535 / per_layer);
+    for (int l0 = l_begin; l0 < l_end; l0 += lpp) {
+      const int rows = min(lpp, l_end - l0) * per_layer;
+      const int64_t base = (int64_t)l0 * H * len * D * ES;
+      const char* __restrict__ ksrc = reinterpret_cast<const char*>(w.k) + base;
+      const char* __restrict__ vsrc = reinterpret_cast<const char*>(w.v) + base;
+      for (int r0 = tid / 16; r0 < rows; r0 += U * RPS) {
+        u32x4 kv[U], vv[U];
+        int gl[U], hh[U], tt[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = r0 + u * RPS;
-        // r -> (layer g, head h, token t); exact for r < 2^16
-        const int g = (int)(((float)r + 0.5f) * inv_pl);
-        const int rem = r - g * per_layer;
-        const int h = (int)(((float)rem + 0.5f) * inv_tc);
-        gl[u] = g;
-        hh[u] = h;
-        tt[u] = rem - h * tc;
-        if (r < rows) {
-          const int64_t e = ((int64_t)(g * H + h) * len + t0 + tt[u]) * D + col;
-          kv[u] = load16(ksrc + e * ES);
-          vv[u] = load16(vsrc + e * ES);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = r0 + u * RPS;
-        if (r < rows) {   // uniform across each 16-lane row
-          u32x4 other;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            other[q] = (unsigned)__builtin_amdgcn_mov_dpp((int)kv[u][q], 0x128, 0xF, 0xF, false);
-          const float2* csr = cs + tt[u] * HALF + fcol;
-          u32x4 out;
-          if constexpr (ES == 4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const unsigned uo = kv[u][e], up = other[e];
-              const float2 r2 = csr[e];
-              out[e] = __float_as_uint(__builtin_fmaf(__uint_as_float(uo), r2.x,
-                                                      __uint_as_float(up) * (sgn * r2.y)));
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const unsigned uo = kv[u][q], up = other[q];
-              const float2 r0c = csr[2 * q], r1c = csr[2 * q + 1];
-              const float y0 = __builtin_fmaf(__uint_as_float(uo << 16), r0c.x,
-                                              __uint_as_float(up << 16) * (sgn * r0c.y));
-              const float y1 = __builtin_fmaf(__uint_as_float(uo & 0xFFFF0000u), r1c.x,
-                                              __uint_as_float(up & 0xFFFF0000u) * (sgn * r1c.y));
-              out[q] = pack_bf16(y0, y1);
-            }
+        for (int u = 0; u < U; ++u) {
+          const int r = r0 + u * RPS;
+          // r -> (layer g, head h, token t); exact for r < 2^16
+          const int g = (int)(((float)r + 0.5f) * inv_pl);
+          const int rem = r - g * per_layer;
+          const int h = (int)(((float)rem + 0.5f) * inv_tc);
+          gl[u] = g;
+          hh[u] = h;
+          tt[u] = rem - h * tc;
+          if (r < rows) {
+            const int64_t e = ((int64_t)(g * H + h) * len + t0 + tt[u]) * D + col;
+            kv[u] = load16(ksrc + e * ES);
+            vv[u] = load16(vsrc + e * ES);
           }
-          const int64_t dst = (int64_t)(l0 + gl[u]) * a.s_layer + slot_off[tt[u]] +
-                              (int64_t)hh[u] * a.s_head + col;
-          store16(kc + dst * ES, out);
-          store16(vc + dst * ES, vv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int r = r0 + u * RPS;
+          if (r < rows) {   // uniform across each 16-lane row
+            u32x4 other;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              other[q] = (unsigned)__builtin_amdgcn_mov_dpp((int)kv[u][q], 0x128, 0xF, 0xF, false);
+            const float2* csr = cs + tt[u] * HALF + fcol;
+            u32x4 out;
+            if constexpr (ES == 4) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const unsigned uo = kv[u][e], up = other[e];
+                const float2 r2 = csr[e];
+                out[e] = __float_as_uint(__builtin_fmaf(__uint_as_float(uo), r2.x,
+                                                        __uint_as_float(up) * (sgn * r2.y)));
+              }
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const unsigned uo = kv[u][q], up = other[q];
+                const float2 r0c = csr[2 * q], r1c = csr[2 * q + 1];
+                const float y0 = __builtin_fmaf(__uint_as_float(uo << 16), r0c.x,
+                                                __uint_as_float(up << 16) * (sgn * r0c.y));
+                const float y1 = __builtin_fmaf(__uint_as_float(uo & 0xFFFF0000u), r1c.x,
+                                                __uint_as_float(up & 0xFFFF0000u) * (sgn * r1c.y));
+                out[q] = pack_bf16(y0, y1);
+              }
+            }
+            const int64_t dst = (int64_t)(l0 + gl[u]) * a.s_layer + slot_off[tt[u]] +
+                                (int64_t)hh[u] * a.s_head + col;
+            store16(kc + dst * ES, out);
+            store16(vc + dst * ES, vv[u]);
+          }
         }
       }
     }
@@ -335,28 +362,43 @@ __global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
   }
 }
 
-template <int ES>
-hipError_t launch_es(const InjectLaunch& a, hipStream_t stream) {
-  if (IS_R16 && a.lanes == 8) {
-    constexpr int G = IS_R16_LAYERS;
-    const unsigned n_groups = (unsigned)((a.n_layers + G - 1) / G);
-    // the item index is grid y: launch at most 65535 items at a time
-    constexpr int32_t kMaxItems = IS_R16_LAYER_FAST ? 65535 : INT32_MAX;
-    for (int32_t i0 = 0; i0 < a.n_items; i0 += kMaxItems) {
-      InjectLaunch part = a;
-      part.work = a.work + i0;
-      part.n_items = a.n_items - i0 < kMaxItems ? a.n_items - i0 : kMaxItems;
-      const dim3 grid16 = IS_R16_LAYER_FAST ? dim3(n_groups, (unsigned)part.n_items)
-                                            : dim3((unsigned)part.n_items, n_groups);
-      hipLaunchKernelGGL((inject_row16<ES, IS_R16_THREADS, G, IS_R16_ROWS, IS_R16_TC>), grid16,
-                         dim3(IS_R16_THREADS), 0, stream, part);
-    }
-    return hipGetLastError();
+template <int ES, int T, int U>
+hipError_t launch_r16(const InjectLaunch& a, hipStream_t stream) {
+  const unsigned n_groups = (unsigned)((a.n_layers + a.layers_per_wg - 1) / a.layers_per_wg);
+  // the item index is grid y: launch at most 65535 items at a time
+  constexpr int32_t kMaxItems = IS_R16_LAYER_FAST ? 65535 : INT32_MAX;
+  for (int32_t i0 = 0; i0 < a.n_items; i0 += kMaxItems) {
+    InjectLaunch part = a;
+    part.work = a.work + i0;
+    part.n_items = a.n_items - i0 < kMaxItems ? a.n_items - i0 : kMaxItems;
+    const dim3 grid16 = IS_R16_LAYER_FAST ? dim3(n_groups, (unsigned)part.n_items)
+                                          : dim3((unsigned)part.n_items, n_groups);
+    hipLaunchKernelGGL((inject_row16<ES, T, U, IS_R16_TC>), grid16, dim3(T), 0, stream, part);
   }
-  const dim3 grid((unsigned)a.n_items, (unsigned)a.n_layers);
-  switch (a.lanes) {
+  return hipGetLastError();
+}
+
+template <int ES>
+hipError_t launch_es(const InjectLaunch& in, hipStream_t stream) {
+  if (IS_R16 && in.lanes == 8) {
+    // Workgroup shape from the mean fact length: rows of one layer of a
+    // fact = kv_heads x length.  Long facts: one layer per 512-lane
+    // workgroup (8 rows in flight per lane).  Short facts: enough layers per
+    // 256-lane workgroup (4 rows in flight per lane) for about
+    // IS_R16_SHORT_ROWS rows.
+    InjectLaunch a = in;
+    const float rows = (float)a.n_heads * (a.mean_len > 1.0f ? a.mean_len : 1.0f);
+    const bool short_facts = rows < (float)IS_R16_SHORT_ROWS;
+    int g = short_facts ? (int)((float)IS_R16_SHORT_ROWS / rows + 0.999f) : 1;
+    if (IS_R16_FIXED_LAYERS > 0) g = IS_R16_FIXED_LAYERS;
+    a.layers_per_wg = g < a.n_layers ? g : a.n_layers;
+    return short_facts ? launch_r16<ES, IS_R16_SHORT_THREADS, IS_R16_SHORT_U>(a, stream)
+                       : launch_r16<ES, IS_R16_THREADS, IS_R16_ROWS>(a, stream);
+  }
+  const dim3 grid((unsigned)in.n_items, (unsigned)in.n_layers);
+  switch (in.lanes) {
 #define IS_CASE(L) \
-    case L: hipLaunchKernelGGL((inject_kernel<ES, L>), grid, dim3(kThreads), 0, stream, a); break;
+    case L: hipLaunchKernelGGL((inject_kernel<ES, L>), grid, dim3(kThreads), 0, stream, in); break;
     IS_CASE(2) IS_CASE(4) IS_CASE(8) IS_CASE(16) IS_CASE(32)
 #undef IS_CASE
     default: return hipErrorInvalidValue;

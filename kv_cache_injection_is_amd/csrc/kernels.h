@@ -26,6 +26,8 @@ struct InjectLaunch {
   int32_t lanes;          // 16-byte chunks per half row
   const int32_t* status;  // device status word: the kernel writes nothing unless it is 0
                           // (null: no check)
+  float mean_len;         // mean injected fact length (tokens): sets the workgroup shape
+  int32_t layers_per_wg;  // derived by launch_inject
 };
 
 hipError_t launch_inject(const InjectLaunch& a, hipStream_t stream);

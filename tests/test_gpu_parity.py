@@ -110,6 +110,26 @@ def test_inject_host_tier(gpu):
         st.destroy()
 
 
+@pytest.mark.parametrize("host_tier", [False, True])
+def test_inject_short_facts_layer_groups(gpu, host_tier):
+    """Facts of 1-3 tokens: a workgroup takes several layers (40 layers, 4
+    kv heads: 16 layers per workgroup, groups of 16, 16 and 8), and with a
+    host tier the host-tier facts take one workgroup for all layers."""
+    w = SMALL_LLAMA.scaled(name="short", n_layers=40, n_kv_heads=4, n_facts=400,
+                           len_dist=("uniform", 1, 3), n_blocks=300, prefix=(0, 40))
+    lens, req_off, flat, prefix, bt = _zipf_problem(w, 12, 20)
+    budget = int(lens[:200].sum()) * w.token_bytes * 2 if host_tier else -1
+    st = Hn.make_store(w, lens, hbm_budget=budget)
+    try:
+        if host_tier:
+            assert (flat >= 200).any() and (flat < 200).any()
+        cache = Hn.make_cache(w)
+        Hn.gpu_inject(st, cache, req_off, flat, prefix, bt)
+        Hn.check_inject_blocks(cache, lens, req_off, flat, prefix, bt, np.arange(w.n_blocks))
+    finally:
+        st.destroy()
+
+
 def test_inject_deterministic_and_position_zero_identity(gpu):
     import torch
     w = SMALL_LLAMA
