@@ -62,11 +62,13 @@ def traffic_from_counters(n_launch_bytes: float):
 
 
 def topk_cold(torch, stream, flush, fn, reps: int) -> float:
-    """Median time of `fn` on `stream`, each call preceded by a 1 GiB write
-    that evicts the L2 and Infinity Cache (HIP events around the call)."""
+    """Median time of `fn` on `stream`, each call preceded by a read of a
+    1 GiB buffer that evicts the L2 and the 256 MB Infinity Cache (HIP events
+    around the call).  A read, not a write: the write-back of a write flush's
+    dirty lines would run during the timed call."""
     times = []
     for i in range(reps):
-        flush.fill_(i & 255)
+        flush.max()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
@@ -905,7 +907,7 @@ def main() -> int:
                  "ms": round(topk_ms, 4), "frac_of_8TBps": round(topk_gbps / HBM_PEAK_GBPS, 4),
                  "ms_cold": round(topk_cold_ms, 4),
                  "note": "ms: back-to-back launches (the 102 MB of embeddings may stay in the "
-                         "256 MB Infinity Cache); ms_cold: median with a 1 GiB write before "
+                         "256 MB Infinity Cache); ms_cold: median with a 1 GiB read before "
                          "each call"},
         "topk_1m": topk_1m,
         "device_path": dev,

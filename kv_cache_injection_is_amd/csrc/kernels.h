@@ -115,10 +115,11 @@ struct TopkLaunch {
   int32_t n_q;
   int32_t k;
   int32_t scan_wgs;       // derived by launch_topk
-  // derived by launch_topk; n_tiles and sample_tiles count scan tiles of
-  // scan_tile facts (the scan kernel's tile: 256, or 128 for the variant
-  // that keeps the queries in registers)
-  int32_t scan_tile;
+  // derived by launch_topk; n_tiles counts stream tiles of scan_tile facts
+  // and sample_tiles sample tiles of sample_tile facts (256 for the staged
+  // scan; 32, 64 or 128 for the variant that keeps the queries in registers)
+  int32_t scan_tile;      // facts per stream tile
+  int32_t sample_tile;    // facts per sample tile
   int64_t n_tiles, sample_n, sample_tiles, n_groups, cand_stride;
   // scratch (see topk_scratch)
   uint16_t* q_pad;        // [n_q][padded_dim] when emb_dim % 64 != 0

@@ -35,18 +35,22 @@
 //                 query tile the launch fills; the query chunk is staged
 //                 with the fact block in a 3-stage ring, and a wave refills
 //                 its own fact rows without waiting for the other waves;
-//   topk_scan_qr  full batches at width 1024 over large stores: each wave
-//                 keeps its 32 query rows in registers for the whole launch
-//                 and scores every fact of a 128-fact tile, the ring (eight
-//                 16 KB stages, seven in flight) holds fact rows only, and
+//   topk_scan_rq  full batches at width 1024: each wave keeps its 32 query
+//                 rows in registers for the whole launch and scores every
+//                 fact of a 32-, 64- or 128-fact tile, the ring (8 or 16
+//                 stages, all but one in flight) holds fact rows only, and
 //                 candidates are staged in LDS until the loop ends (see
-//                 below).
+//                 below).  Sample and stream may use different tile sizes:
+//                 every fact's score is the same MFMA chain in both.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
 
 #ifndef IS_TOPK_RESIDENT
 #define IS_TOPK_RESIDENT 1   // full batches at width 1024 keep their queries in registers
+#endif
+#ifndef IS_TOPK_SAMPLE_WGS
+#define IS_TOPK_SAMPLE_WGS 128   // workgroups the sample scan should at least fill
 #endif
 
 namespace is {
@@ -340,34 +344,48 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
   }
 }
 
-// Scan variant for full query batches (65..128 queries) at width 1024 over
-// stores of kResidentMinFacts or more (below it a workgroup's chunks are too
-// few to fill the deeper ring).
+// Scan variant for full query batches (65..128 queries) at width 1024.
 // The query rows are the same for every tile, so instead of re-staging them
 // through LDS for every chunk, each wave keeps its own 32 query rows -- all
 // 1024 dims, 256 registers per lane -- for the whole launch, and the LDS
-// ring holds fact rows only: eight stages of a 128-fact x 64-dim block
-// (16 KB, one half of a stored 256 x 64 block), seven of them in flight
-// while one is scored.  Every wave scores all 128 facts of a stage against
-// its 32 queries (four v_mfma_f32_32x32x16_f16 row tiles per k-step), so all
-// waves read every stage and one barrier per chunk both publishes a stage
-// and frees the one scored before it.  With 16 chunks per tile and 8 stages
-// the ring slot of a chunk is fixed by its index in the tile, which keeps
-// the query registers and the ring addressing static.
-constexpr int kRFT = 128;                       // facts per tile
-constexpr int kRChunks = 16;                    // 64-dim chunks of a 1024-wide row
-constexpr int kRStages = 8;
-constexpr int kRPieces = kRFT * kKC / 8;        // 16-byte pieces of a stage
-constexpr int kRDma = kRPieces / 64 / kWaves;   // transfers per wave per stage
-static_assert(kRChunks % kRStages == 0, "ring slot must be static per chunk");
-constexpr int64_t kResidentMinFacts = (int64_t)4 * kTopkMaxScanWG * kRFT;   // 131,072
+// ring holds fact rows only: stages of an FT-fact x 64-dim block (FT = 32,
+// 64 or 128 facts: part of a stored 256 x 64 block), all but one of them in
+// flight while one is scored.  Every wave scores all FT facts of a stage
+// against its 32 queries (FT / 32 v_mfma_f32_32x32x16_f16 row tiles per
+// k-step), so all waves read every stage and one barrier per chunk both
+// publishes a stage and frees the one scored before it.  With 16 chunks per
+// tile and 8 or 16 stages the ring slot of a chunk is fixed by its index in
+// the tile, which keeps the query registers and the ring addressing static.
+// Small tiles spread a small store (or the threshold sample) over many
+// workgroups; large ones cost fewer barriers per byte.
+//
+// A fact's score is the same chain of MFMAs in every tile size and in
+// topk_scan: k-step s of chunk c multiplies dims c*64 + (2s + grp)*8 .. +8 of
+// both operands (fact as the A row, query as the B column), chunks in
+// order, starting from a zero accumulator.  A sample scanned with one tile
+// size and a stream scanned with another therefore score every fact bit for
+// bit alike, which keeps the bound exact.
+constexpr int kRChunks = 16;   // 64-dim chunks of a 1024-wide row
+template <int FT>
+struct Rq {
+  static constexpr int kStages = FT == 128 ? 8 : 16;
+  static constexpr int kPieces = FT * kKC / 8;        // 16-byte pieces of a stage
+  static constexpr int kDma = kPieces / 64 / kWaves;  // transfers per wave per stage
+  static constexpr int kRows = FT / 32;               // MFMA row tiles per stage
+  static_assert(kRChunks % kStages == 0, "ring slot must be static per chunk");
+  static_assert(kDma >= 1 && (kStages - 2) * kDma < 64, "vmcnt range");
+  static_assert(kFT % FT == 0, "a tile is a part of a stored 256-fact block");
+};
+// Stores at least this large stream in 128-fact tiles (four or more per
+// workgroup); smaller ones in 32-fact tiles, which keep every workgroup busy.
+constexpr int64_t kResidentBigFacts = (int64_t)4 * kTopkMaxScanWG * 128;   // 131,072
 static_assert(kQB == kWaves * 32, "one 32-query tile per wave");
 
 // Candidates found during the stream are staged in LDS and written out
 // after the loop: a global store counts in vmcnt like the ring's transfers,
-// and, issued behind seven chunks in flight, it would make every ring wait
-// of the next steps wait for that much more.  Each wave owns its queries,
-// so it also owns their candidates: a query's running count lives in the
+// and, issued behind the chunks in flight, it would make every ring wait of
+// the next steps wait for that much more.  Each wave owns its queries, so
+// it also owns their candidates: a query's running count lives in the
 // registers of its two lanes, and each wave fills its own part of the
 // staging area, slots taken by a ballot prefix sum (no atomics).  An
 // entry's destination is (query << 25) | position in the query's region;
@@ -375,8 +393,9 @@ static_assert(kQB == kWaves * 32, "one 32-query tile per wave");
 constexpr int kCandWave = 512;   // staged candidates per wave
 constexpr int kPosBits = 25;
 
-struct ScanSmemQR {
-  u32x4 e[kRStages][kRPieces];
+template <int FT>
+struct ScanSmemRq {
+  u32x4 e[Rq<FT>::kStages][Rq<FT>::kPieces];
   uint64_t ckey[kWaves][kCandWave];
   uint32_t cdst[kWaves][kCandWave];
 };
@@ -397,23 +416,25 @@ __device__ __forceinline__ uint32_t wave_prefix(uint32_t n, uint32_t& total) {
   return pre;
 }
 
-// Waits until at most 4 * n of this wave's ring transfers are in flight.
-__device__ __forceinline__ void wait_chunks(int n) {
-  static_assert(kRDma == 4, "wait counts assume four transfers per stage");
-  switch (n) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<4>(); break;
-    case 2: wait_vm<8>(); break;
-    case 3: wait_vm<12>(); break;
-    case 4: wait_vm<16>(); break;
-    case 5: wait_vm<20>(); break;
-    default: wait_vm<24>(); break;
+// Waits until at most D * min(n, N) of this wave's transfers are in flight
+// (n is a constant once the chunk loop is unrolled).
+template <int D, int N>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (N <= 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= N) {
+      wait_vm<D * N>();
+      return;
+    }
+    wait_stages<D, N - 1>(n);
   }
 }
 
-template <bool kSample>
-__global__ __launch_bounds__(kThreads) void topk_scan_qr(TopkLaunch a) {
-  __shared__ ScanSmemQR sm;
+template <bool kSample, int FT>
+__global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
+  using R = Rq<FT>;
+  __shared__ ScanSmemRq<FT> sm;
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
@@ -423,13 +444,12 @@ __global__ __launch_bounds__(kThreads) void topk_scan_qr(TopkLaunch a) {
   const int w = (int)blockIdx.x;
   const int64_t n_tiles = kSample ? a.sample_tiles : a.n_tiles;
   const int my_tiles = (int)((n_tiles - w + G - 1) / G);
-  const int total = my_tiles * kRChunks;
-  const int64_t edge_tile = (a.n_facts - 1) / kRFT;
+  const int64_t edge_tile = (a.n_facts - 1) / FT;
   const int q = wave * 32 + row;   // this lane's query (column of every score tile)
   const bool q_ok = q < a.n_q;
   const float tau = (!kSample && q_ok) ? a.tau[q] : 0.f;
-  const uint64_t region0 = (uint64_t)region_tile(w, n_tiles, G) * kRFT;
-  const bool stage_ok = (int64_t)my_tiles * kRFT <= ((int64_t)1 << kPosBits);
+  const uint64_t region0 = (uint64_t)region_tile(w, n_tiles, G) * FT;
+  const bool stage_ok = (int64_t)my_tiles * FT <= ((int64_t)1 << kPosBits);
   uint32_t q_count = 0;    // candidates of this lane's query so far (both its lanes)
   uint32_t staged = 0;     // this wave's staging slots used (wave-uniform)
 
@@ -445,20 +465,21 @@ __global__ __launch_bounds__(kThreads) void topk_scan_qr(TopkLaunch a) {
   }
 
   const uint32_t e_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.e[0][0];
-  // Issue cursor: tile et (in 128-fact tiles), chunk ec.  Tile et is half
-  // et & 1 of stored 256-fact tile et >> 1, whose chunk ec is one 32 KB span.
+  // Issue cursor: tile et (in FT-fact tiles), chunk ec.  Tile et is part
+  // et % P of stored 256-fact tile et / P, whose chunk ec is one 32 KB span.
+  constexpr int P = kFT / FT;
   int64_t et = w;
   int ec = 0;
   auto issue = [&](int slot_stage) {
     const uint16_t* blk =
-        a.emb + (((et >> 1) * kRChunks + ec) * kFT + (et & 1) * kRFT) * (int64_t)kKC;
+        a.emb + (((et / P) * kRChunks + ec) * kFT + (et % P) * FT) * (int64_t)kKC;
 #pragma unroll
-    for (int i = 0; i < kRDma; ++i) {
-      const int s0 = (wave * kRDma + i) * 64;
+    for (int i = 0; i < R::kDma; ++i) {
+      const int s0 = (wave * R::kDma + i) * 64;
       const int slot = s0 + lane;
       const int r = slot >> 3, p = (slot & 7) ^ ((r >> 1) & 7);
       dma16(blk + r * kKC + p * 8,
-            __builtin_amdgcn_readfirstlane(e_lds + (uint32_t)((slot_stage * kRPieces + s0) * 16)));
+            __builtin_amdgcn_readfirstlane(e_lds + (uint32_t)((slot_stage * R::kPieces + s0) * 16)));
     }
     if (++ec == kRChunks) {
       ec = 0;
@@ -466,51 +487,47 @@ __global__ __launch_bounds__(kThreads) void topk_scan_qr(TopkLaunch a) {
     }
   };
 
-  float16v acc[kRFT / 32];
+  float16v acc[R::kRows];
+  // The tile's epilogue, one 32-fact row tile at a time (16 scores per lane
+  // live at once).  Element e of a lane's fragment of row tile ft is fact
+  // f0 + 8 * (e / 4) + e % 4, f0 = t * FT + ft * 32 + 4 * grp.
   auto emit = [&](int64_t t) {
-    float v[kRFT / 32][16];
-    uint32_t m[kRFT / 32];
-    uint32_t n = 0;
 #pragma unroll
-    for (int ft = 0; ft < kRFT / 32; ++ft) {
-      // element e of a lane's fragment is fact f0 + 8 * (e / 4) + e % 4
-      const int64_t f0 = t * kRFT + ft * 32 + 4 * grp;
+    for (int ft = 0; ft < R::kRows; ++ft) {
+      const int64_t f0 = t * FT + ft * 32 + 4 * grp;
+      float v[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[ft][e] = acc[ft][e];
-      if (t == edge_tile) mask_padding(v[ft], (int32_t)(a.n_facts - f0));   // uniform branch
-      float mx = v[ft][0];
+      for (int e = 0; e < 16; ++e) v[e] = acc[ft][e];
+      if (t == edge_tile) mask_padding(v, (int32_t)(a.n_facts - f0));   // uniform branch
+      float mx = v[0];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[ft][e]);
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
       if (kSample) {
         if (q_ok) {
-          const int64_t gi = (t * (kRFT / 32) + ft) * 2 + grp;
+          const int64_t gi = (t * R::kRows + ft) * 2 + grp;
           a.gmax[(int64_t)q * a.n_groups + gi] = (mx == -INFINITY) ? 0u : ord_of(mx);
         }
-      } else {
-        m[ft] = 0;
-        if (q_ok && mx >= tau) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) m[ft] |= (v[ft][e] >= tau) ? (1u << e) : 0u;
-        }
-        n += (uint32_t)__builtin_popcount(m[ft]);
+        continue;
       }
-    }
-    if (kSample || !__any(n != 0)) return;
-    // positions in the query's region: the grp 0 lane's candidates first
-    const uint32_t n_pair = __shfl_xor(n, 32);
-    uint32_t pos = q_count + (grp ? n_pair : 0u);
-    q_count += n + n_pair;
-    uint32_t wave_n;
-    uint32_t slot = staged + wave_prefix(n, wave_n);
-    staged += wave_n;
-    uint64_t* direct = a.cand + (int64_t)q * a.cand_stride + region0;
+      uint32_t m = 0;
+      if (q_ok && mx >= tau) {
 #pragma unroll
-    for (int ft = 0; ft < kRFT / 32; ++ft) {
-      const uint32_t f0 = (uint32_t)(t * kRFT + ft * 32 + 4 * grp);
+        for (int e = 0; e < 16; ++e) m |= (v[e] >= tau) ? (1u << e) : 0u;
+      }
+      if (!__any(m != 0)) continue;
+      // positions in the query's region: the grp 0 lane's candidates first
+      const uint32_t n = (uint32_t)__builtin_popcount(m);
+      const uint32_t n_pair = __shfl_xor(n, 32);
+      uint32_t pos = q_count + (grp ? n_pair : 0u);
+      q_count += n + n_pair;
+      uint32_t wave_n;
+      uint32_t slot = staged + wave_prefix(n, wave_n);
+      staged += wave_n;
+      uint64_t* direct = a.cand + (int64_t)q * a.cand_stride + region0;
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if (m[ft] & (1u << e)) {
-          const uint64_t key = key_of(ord_of(v[ft][e]), f0 + 8 * (e / 4) + (e % 4));
+        if (m & (1u << e)) {
+          const uint64_t key = key_of(ord_of(v[e]), (uint32_t)f0 + 8 * (e / 4) + (e % 4));
           if (stage_ok && slot < (uint32_t)kCandWave) {
             sm.ckey[wave][slot] = key;
             sm.cdst[wave][slot] = ((uint32_t)q << kPosBits) | pos;
@@ -525,32 +542,32 @@ __global__ __launch_bounds__(kThreads) void topk_scan_qr(TopkLaunch a) {
 
   // One chunk: `after` = chunks of this workgroup still to come after it
   // (a constant once the chunk loop is unrolled; kRChunks for every tile
-  // but the last).  All 16 fragments of the stage are read before the 16
-  // MFMAs, so the chunk pays one LDS latency rather than one per MFMA.
+  // but the last).  All fragments of the stage are read before its MFMAs,
+  // so the chunk pays one LDS latency rather than one per MFMA.
   auto step = [&](int c, int after) {
-    wait_chunks(after < kRStages - 2 ? after : kRStages - 2);
+    wait_stages<R::kDma, R::kStages - 2>(after);
     ring_barrier();   // chunk c landed for every wave; the previous stage is free
-    if (after >= kRStages - 1) issue((c + kRStages - 1) % kRStages);
-    const u32x4* es = sm.e[c % kRStages];
-    half8 av[kKC / 16][kRFT / 32];
+    if (after >= R::kStages - 1) issue((c + R::kStages - 1) % R::kStages);
+    const u32x4* es = sm.e[c % R::kStages];
+    half8 av[kKC / 16][R::kRows];
 #pragma unroll
     for (int s = 0; s < kKC / 16; ++s)
 #pragma unroll
-      for (int ft = 0; ft < kRFT / 32; ++ft)
+      for (int ft = 0; ft < R::kRows; ++ft)
         av[s][ft] = __builtin_bit_cast(half8, es[piece_slot(ft * 32 + row, 2 * s + grp)]);
     __builtin_amdgcn_sched_barrier(0);
     const float16v zero = {};
 #pragma unroll
     for (int s = 0; s < kKC / 16; ++s)
 #pragma unroll
-      for (int ft = 0; ft < kRFT / 32; ++ft)
+      for (int ft = 0; ft < R::kRows; ++ft)
         acc[ft] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
             av[s][ft], qv[c * 4 + s], (c == 0 && s == 0) ? zero : acc[ft], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // total >= 16 > kRStages - 1: the prologue always fills the ring.
+  // total >= 16 >= kStages: the prologue always fills the ring.
 #pragma unroll
-  for (int g = 0; g < kRStages - 1; ++g) issue(g);
+  for (int g = 0; g < R::kStages - 1; ++g) issue(g);
   int64_t ct = w;
   for (int i = 0; i + 1 < my_tiles; ++i) {
 #pragma unroll
@@ -698,7 +715,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
     }
   };
   if (total <= (uint32_t)kStage64) {
-    for (uint32_t i = 0; i < cnt; ++i) keys[excl + i] = mine[i];
+    // eight independent loads in flight per thread
+    for (uint32_t i0 = 0; i0 < cnt; i0 += 8) {
+      uint64_t t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = i0 + j < cnt ? mine[i0 + j] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (i0 + j < cnt) keys[excl + i0 + j] = t[j];
+    }
     __syncthreads();
     const uint64_t thr = kth_largest<uint64_t>([&](auto fn) {
       for (uint32_t i = tid; i < total; i += kSelThreads) fn(keys[i]);
@@ -823,18 +848,28 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
   TopkLaunch a = in;
   const int32_t padded = topk_padded_dim(a.emb_dim);
   // query tiles of 32 the launch fills: 1, 2 or 4.  Full batches at width
-  // 1024 over large stores keep their queries in registers (128-fact tiles);
-  // below kResidentMinFacts (4 tiles per workgroup) a workgroup's chunks are
-  // too few to fill the deeper ring, and the staged scan's 32 KB steps are
-  // fewer.  Sample and stream scan always use the same kernel.
+  // 1024 keep their queries in registers: the stream in 128-fact tiles from
+  // 131,072 facts on, in 32-fact tiles below (every workgroup busy), the
+  // sample in the largest tile that still gives it IS_TOPK_SAMPLE_WGS
+  // workgroups.  Other batches and widths use the staged scan for both.
   const int qt = a.n_q <= 32 ? 1 : a.n_q <= 64 ? 2 : 4;
-  const bool resident = IS_TOPK_RESIDENT && qt == 4 && padded == kRChunks * kKC &&
-                        a.n_facts >= kResidentMinFacts;
-  a.scan_tile = resident ? kRFT : kFT;
-  a.n_tiles = (a.n_facts + a.scan_tile - 1) / a.scan_tile;
+  const bool resident = IS_TOPK_RESIDENT && qt == 4 && padded == kRChunks * kKC;
   a.sample_n = topk_sample_size(a.n_facts);
-  a.sample_tiles = (a.sample_n + a.scan_tile - 1) / a.scan_tile;
-  a.n_groups = a.sample_tiles * (a.scan_tile / 16);   // groups of 16 facts
+  int ft_stream = kFT, ft_sample = kFT;
+  if (resident) {
+    ft_stream = a.n_facts >= kResidentBigFacts ? 128 : 32;
+    ft_sample = 32;
+    for (int f : {128, 64})
+      if ((a.sample_n + f - 1) / f >= IS_TOPK_SAMPLE_WGS) {
+        ft_sample = f;
+        break;
+      }
+  }
+  a.scan_tile = ft_stream;
+  a.sample_tile = ft_sample;
+  a.n_tiles = (a.n_facts + ft_stream - 1) / ft_stream;
+  a.sample_tiles = (a.sample_n + ft_sample - 1) / ft_sample;
+  a.n_groups = a.sample_tiles * (ft_sample / 16);   // groups of 16 facts
   a.cand_stride = topk_padded_facts(a.n_facts);
   a.scan_wgs = (int32_t)(a.n_tiles < kTopkMaxScanWG ? a.n_tiles : kTopkMaxScanWG);
   if (padded != a.emb_dim) {
@@ -847,9 +882,16 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
   const int sample_wgs = (int)(a.sample_tiles < kTopkMaxScanWG ? a.sample_tiles : kTopkMaxScanWG);
   auto scan = [&](bool sample, unsigned wgs) {
     const dim3 g(wgs), b(kThreads);
+    const int ft = sample ? ft_sample : ft_stream;
     if (resident) {
-      if (sample) hipLaunchKernelGGL(topk_scan_qr<true>, g, b, 0, stream, a);
-      else hipLaunchKernelGGL(topk_scan_qr<false>, g, b, 0, stream, a);
+      if (sample) {
+        if (ft == 128) hipLaunchKernelGGL((topk_scan_rq<true, 128>), g, b, 0, stream, a);
+        else if (ft == 64) hipLaunchKernelGGL((topk_scan_rq<true, 64>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((topk_scan_rq<true, 32>), g, b, 0, stream, a);
+      } else {
+        if (ft == 128) hipLaunchKernelGGL((topk_scan_rq<false, 128>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((topk_scan_rq<false, 32>), g, b, 0, stream, a);
+      }
     } else if (sample) {
       if (qt == 1) hipLaunchKernelGGL((topk_scan<true, 1>), g, b, 0, stream, a);
       else if (qt == 2) hipLaunchKernelGGL((topk_scan<true, 2>), g, b, 0, stream, a);
