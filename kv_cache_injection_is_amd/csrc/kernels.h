@@ -115,6 +115,7 @@ struct TopkLaunch {
   int32_t n_q;
   int32_t k;
   int32_t scan_wgs;       // derived by launch_topk
+  int32_t fuse_tau;       // derived by launch_topk: the stream scan finds the bounds
   // derived by launch_topk; n_tiles counts stream tiles of scan_tile facts
   // and sample_tiles sample tiles of sample_tile facts (256 for the staged
   // scan; 32, 64 or 128 for the variant that keeps the queries in registers)

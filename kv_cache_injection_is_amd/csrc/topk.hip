@@ -49,8 +49,17 @@
 #ifndef IS_TOPK_RESIDENT
 #define IS_TOPK_RESIDENT 1   // full batches at width 1024 keep their queries in registers
 #endif
+#ifndef IS_TOPK_SMALL_STREAM_FT
+#define IS_TOPK_SMALL_STREAM_FT 32   // stream tile (facts) of full batches below 131,072 facts
+#endif
+#ifndef IS_TOPK_BIG_STREAM_FT
+#define IS_TOPK_BIG_STREAM_FT 32     // ... and from 131,072 facts on
+#endif
+static_assert((IS_TOPK_SMALL_STREAM_FT == 32 || IS_TOPK_SMALL_STREAM_FT == 64) &&
+                  (IS_TOPK_BIG_STREAM_FT == 32 || IS_TOPK_BIG_STREAM_FT == 64),
+              "stream tiles of 32 or 64 facts (128-fact tiles spill the spread candidate test)");
 #ifndef IS_TOPK_SAMPLE_WGS
-#define IS_TOPK_SAMPLE_WGS 128   // workgroups the sample scan should at least fill
+#define IS_TOPK_SAMPLE_WGS 192   // workgroups the sample scan should at least fill
 #endif
 
 namespace is {
@@ -91,6 +100,38 @@ __device__ __forceinline__ float float_of(uint32_t o) {
 // Larger key = better: score first, then the lower id.
 __device__ __forceinline__ uint64_t key_of(uint32_t ord, uint32_t id) {
   return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+
+// The stream bound from the k-th largest sample group maximum (an order
+// code; 0 marks an empty group: fewer than k groups reached it), lowered by
+// a hair so that rounding cannot drop a fact that ties it.
+__device__ __forceinline__ float tau_of_code(uint32_t kth) {
+  const float t = kth == 0 ? -INFINITY : float_of(kth);
+  return kth == 0 ? t : t - (fabsf(t) * 0x1p-20f + 0x1p-100f);
+}
+
+// The k-th largest of the n (<= 1024) order codes at src, by one wave: bit
+// by bit from the top, a bit is kept when at least k codes reach the prefix
+// with it set, which ends at the largest x that k codes reach.  0 when
+// fewer than k codes are nonzero.
+constexpr int kWaveKthMax = 1024;
+__device__ uint32_t wave_kth_code(const uint32_t* __restrict__ src, int64_t n, int k) {
+  const int lane = threadIdx.x & 63;
+  const int slots = (int)((n + 63) / 64);
+  uint32_t v[kWaveKthMax / 64];
+#pragma unroll
+  for (int j = 0; j < kWaveKthMax / 64; ++j)
+    v[j] = (j < slots && lane + 64 * j < n) ? src[lane + 64 * j] : 0u;
+  uint32_t prefix = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = prefix | (1u << b);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kWaveKthMax / 64; ++j)
+      if (j < slots) cnt += (uint32_t)__builtin_popcountll(__ballot(v[j] >= cand));
+    if (cnt >= (uint32_t)k) prefix = cand;
+  }
+  return prefix;
 }
 
 // First tile of workgroup w when n_tiles tiles are dealt round-robin to G
@@ -355,7 +396,8 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
 // k-step), so all waves read every stage and one barrier per chunk both
 // publishes a stage and frees the one scored before it.  With 16 chunks per
 // tile and 8 or 16 stages the ring slot of a chunk is fixed by its index in
-// the tile, which keeps the query registers and the ring addressing static.
+// the tile, which keeps the query registers and the ring addressing static
+// (a ring slot taken from a running count measured a quarter slower).
 // Small tiles spread a small store (or the threshold sample) over many
 // workgroups; large ones cost fewer barriers per byte.
 //
@@ -398,6 +440,8 @@ struct ScanSmemRq {
   u32x4 e[Rq<FT>::kStages][Rq<FT>::kPieces];
   uint64_t ckey[kWaves][kCandWave];
   uint32_t cdst[kWaves][kCandWave];
+  uint32_t qcount[32];   // shared-query mode: candidates per query so far
+  float qtau[kWaves];    // shared-query mode with fuse_tau: each query's bound
 };
 
 // Exclusive prefix sum over the wave of n (0 <= n <= 64) and the wave's
@@ -431,9 +475,15 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
-template <bool kSample, int FT>
+// kShared: batches of at most 32 queries.  Every wave holds the same 32
+// query rows (rows past n_q are zero and load nothing) and scores its own
+// 32-fact row tile of each 128-fact stage, so one query's candidates come
+// from all four waves and take their positions from an LDS counter.
+template <bool kSample, int FT, bool kShared>
 __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   using R = Rq<FT>;
+  static_assert(!kShared || R::kRows == kWaves, "shared queries: one row tile per wave");
+  constexpr int kRowsW = kShared ? 1 : R::kRows;   // row tiles a wave scores per stage
   __shared__ ScanSmemRq<FT> sm;
   const int tid = threadIdx.x;
   const int wave = tid / 64;
@@ -445,24 +495,22 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   const int64_t n_tiles = kSample ? a.sample_tiles : a.n_tiles;
   const int my_tiles = (int)((n_tiles - w + G - 1) / G);
   const int64_t edge_tile = (a.n_facts - 1) / FT;
-  const int q = wave * 32 + row;   // this lane's query (column of every score tile)
+  const int q = (kShared ? 0 : wave * 32) + row;   // this lane's query (column of every score tile)
   const bool q_ok = q < a.n_q;
-  const float tau = (!kSample && q_ok) ? a.tau[q] : 0.f;
+  // the bound: from the threshold kernel, or (fuse_tau: at most four
+  // queries, shared query tile) found below by wave q from the sample
+  const bool fuse = kShared && !kSample && a.fuse_tau;
+  float tau = (!kSample && !fuse && q_ok) ? a.tau[q] : 0.f;
   const uint64_t region0 = (uint64_t)region_tile(w, n_tiles, G) * FT;
   const bool stage_ok = (int64_t)my_tiles * FT <= ((int64_t)1 << kPosBits);
   uint32_t q_count = 0;    // candidates of this lane's query so far (both its lanes)
   uint32_t staged = 0;     // this wave's staging slots used (wave-uniform)
 
-  // k-step s of chunk c multiplies dims c*64 + (2s + grp)*8 .. +8 of both
-  // operands (the dot product is order-free in k); rows past n_q take row 0
-  // and their scores are never used.
-  half8 qv[kRChunks * 4];
-  {
-    const uint16_t* src = a.q + (int64_t)(q_ok ? q : 0) * (kRChunks * kKC) + grp * 8;
-#pragma unroll
-    for (int j = 0; j < kRChunks * 4; ++j)
-      qv[j] = *reinterpret_cast<const half8*>(src + j * 16);
+  if (kShared) {
+    if (tid < 32) sm.qcount[tid] = 0;
+    __syncthreads();
   }
+  half8 qv[kRChunks * 4];   // this lane's query row, loaded after the ring prologue
 
   const uint32_t e_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.e[0][0];
   // Issue cursor: tile et (in FT-fact tiles), chunk ec.  Tile et is part
@@ -487,17 +535,18 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
     }
   };
 
-  float16v acc[R::kRows];
+  float16v acc[kRowsW];
   // The tile's epilogue, one 32-fact row tile at a time (16 scores per lane
   // live at once).  Element e of a lane's fragment of row tile ft is fact
   // f0 + 8 * (e / 4) + e % 4, f0 = t * FT + ft * 32 + 4 * grp.
   auto emit = [&](int64_t t) {
 #pragma unroll
-    for (int ft = 0; ft < R::kRows; ++ft) {
+    for (int fw = 0; fw < kRowsW; ++fw) {
+      const int ft = kShared ? wave : fw;   // row tile of the stage
       const int64_t f0 = t * FT + ft * 32 + 4 * grp;
       float v[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[e] = acc[ft][e];
+      for (int e = 0; e < 16; ++e) v[e] = acc[fw][e];
       if (t == edge_tile) mask_padding(v, (int32_t)(a.n_facts - f0));   // uniform branch
       float mx = v[0];
 #pragma unroll
@@ -518,8 +567,9 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
       // positions in the query's region: the grp 0 lane's candidates first
       const uint32_t n = (uint32_t)__builtin_popcount(m);
       const uint32_t n_pair = __shfl_xor(n, 32);
-      uint32_t pos = q_count + (grp ? n_pair : 0u);
-      q_count += n + n_pair;
+      uint32_t base = 0;
+      if (grp == 0 && n + n_pair != 0) base = atomicAdd(&sm.qcount[row], n + n_pair);
+      uint32_t pos = (uint32_t)__shfl((int)base, row) + (grp ? n_pair : 0u);
       uint32_t wave_n;
       uint32_t slot = staged + wave_prefix(n, wave_n);
       staged += wave_n;
@@ -540,47 +590,169 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
     }
   };
 
+  // Batch stream epilogue.  Candidates are rare (a few per 32 x 32 row
+  // tile), so the wave takes one ballot per fragment element: an element no
+  // lane keeps costs a compare and a scalar branch, a kept one a few
+  // instructions.  `capture` keeps a tile's scores (padding masked) and
+  // notes which row tiles hold any candidate; `drain(e)` takes element e of
+  // those row tiles.  A query's two lanes see each other's bit in the
+  // ballot, which orders their candidates (the grp 0 lane's first).
+  float dv[kRowsW][16];   // scores of the captured tile
+  int64_t d_t = 0;        // the captured tile
+  uint32_t d_any = 0;     // bit fw: row tile fw of the captured tile has candidates
+  auto capture = [&](int64_t t) {
+    d_t = t;
+    d_any = 0;
+#pragma unroll
+    for (int fw = 0; fw < kRowsW; ++fw) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dv[fw][e] = acc[fw][e];
+      if (t == edge_tile) mask_padding(dv[fw], (int32_t)(a.n_facts - (t * FT + fw * 32 + 4 * grp)));
+      float mx = dv[fw][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, dv[fw][e]);
+      if (__any(q_ok && mx >= tau)) d_any |= 1u << fw;
+    }
+  };
+  auto drain = [&](int e) {
+#pragma unroll
+    for (int fw = 0; fw < kRowsW; ++fw) {
+      if (!(d_any & (1u << fw))) continue;   // uniform
+      const bool hit = q_ok && dv[fw][e] >= tau;
+      const uint64_t bal = __ballot(hit);
+      if (bal == 0) continue;
+      const uint32_t b_pair = (uint32_t)(bal >> (lane ^ 32)) & 1u;
+      const uint32_t pos = q_count + (grp ? b_pair : 0u);
+      q_count += (uint32_t)hit + b_pair;
+      if (hit) {
+        const uint32_t slot = staged + __builtin_amdgcn_mbcnt_hi(
+                                           (uint32_t)(bal >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        const uint32_t f = (uint32_t)(d_t * FT) + fw * 32 + 4 * grp + 8 * (e / 4) + (e % 4);
+        const uint64_t key = key_of(ord_of(dv[fw][e]), f);
+        if (stage_ok && slot < (uint32_t)kCandWave) {
+          sm.ckey[wave][slot] = key;
+          sm.cdst[wave][slot] = ((uint32_t)q << kPosBits) | pos;
+        } else {
+          a.cand[(int64_t)q * a.cand_stride + region0 + pos] = key;
+        }
+      }
+      staged += (uint32_t)__builtin_popcountll(bal);
+    }
+  };
+
   // One chunk: `after` = chunks of this workgroup still to come after it
   // (a constant once the chunk loop is unrolled; kRChunks for every tile
   // but the last).  All fragments of the stage are read before its MFMAs,
   // so the chunk pays one LDS latency rather than one per MFMA.
-  auto step = [&](int c, int after) {
-    wait_stages<R::kDma, R::kStages - 2>(after);
-    ring_barrier();   // chunk c landed for every wave; the previous stage is free
-    if (after >= R::kStages - 1) issue((c + R::kStages - 1) % R::kStages);
+  //
+  // The fragments of chunk c + 1 are read while chunk c's MFMAs run, so a
+  // chunk costs a barrier and its MFMA chain, not also an LDS latency: step
+  // c waits until chunk c + 1 has landed, passes the barrier (which also
+  // tells that every wave is done with chunk c - 1, whose fragments were
+  // read a step earlier), refills chunk c - 1's slot, reads chunk c + 1 and
+  // scores chunk c from the fragments read before.
+  half8 av[kKC / 16][kRowsW];   // fragments of the chunk being scored
+  auto read_frags = [&](int c, half8 (&dst)[kKC / 16][kRowsW]) {
     const u32x4* es = sm.e[c % R::kStages];
-    half8 av[kKC / 16][R::kRows];
 #pragma unroll
     for (int s = 0; s < kKC / 16; ++s)
 #pragma unroll
-      for (int ft = 0; ft < R::kRows; ++ft)
-        av[s][ft] = __builtin_bit_cast(half8, es[piece_slot(ft * 32 + row, 2 * s + grp)]);
+      for (int fw = 0; fw < kRowsW; ++fw)
+        dst[s][fw] = __builtin_bit_cast(
+            half8, es[piece_slot((kShared ? wave : fw) * 32 + row, 2 * s + grp)]);
+  };
+  auto step = [&](int c, int after) {
+    half8 nx[kKC / 16][kRowsW];
+    if (after >= 1) {
+      wait_stages<R::kDma, R::kStages - 3>(after - 1);
+      ring_barrier();   // chunk c + 1 landed for every wave; chunk c - 1's slot is free
+      if (after >= R::kStages - 1) issue((c + R::kStages - 1) % R::kStages);
+      read_frags((c + 1) % kRChunks, nx);
+    }
     __builtin_amdgcn_sched_barrier(0);
     const float16v zero = {};
 #pragma unroll
     for (int s = 0; s < kKC / 16; ++s)
 #pragma unroll
-      for (int ft = 0; ft < R::kRows; ++ft)
-        acc[ft] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            av[s][ft], qv[c * 4 + s], (c == 0 && s == 0) ? zero : acc[ft], 0, 0, 0);
+      for (int fw = 0; fw < kRowsW; ++fw)
+        acc[fw] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            av[s][fw], qv[c * 4 + s], (c == 0 && s == 0) ? zero : acc[fw], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
+    if (after >= 1) {
+#pragma unroll
+      for (int s = 0; s < kKC / 16; ++s)
+#pragma unroll
+        for (int fw = 0; fw < kRowsW; ++fw) av[s][fw] = nx[s][fw];
+    }
   };
-  // total >= 16 >= kStages: the prologue always fills the ring.
+  // total >= 16 >= kStages: the prologue always fills the ring.  It is
+  // issued before the query rows are loaded, so the first stages stream in
+  // while the queries arrive.
 #pragma unroll
   for (int g = 0; g < R::kStages - 1; ++g) issue(g);
-  int64_t ct = w;
-  for (int i = 0; i + 1 < my_tiles; ++i) {
+  // k-step s of chunk c multiplies dims c*64 + (2s + grp)*8 .. +8 of both
+  // operands (the dot product is order-free in k).  Rows past n_q are zero,
+  // load nothing, and their scores are never used.
+  if (q_ok) {
+    const uint16_t* src = a.q + (int64_t)q * (kRChunks * kKC) + grp * 8;
 #pragma unroll
-    for (int c = 0; c < kRChunks; ++c) step(c, kRChunks);
-    emit(ct);
-    ct += G;
+    for (int j = 0; j < kRChunks * 4; ++j)
+      qv[j] = *reinterpret_cast<const half8*>(src + j * 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRChunks * 4; ++j) qv[j] = half8{};
   }
+  if (kShared && !kSample) {
+    if (fuse) {
+      // while the ring's first stages land: wave w finds query w's bound
+      if (wave < a.n_q) {
+        const float t = tau_of_code(
+            wave_kth_code(a.gmax + (int64_t)wave * a.n_groups, a.n_groups, a.k));
+        if (lane == 0) sm.qtau[wave] = t;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the bound is in LDS before the barrier
+    }
+  }
+  // chunk 0's fragments
+  wait_vm<R::kDma * (R::kStages - 2)>();
+  ring_barrier();
+  if (fuse && q_ok) tau = sm.qtau[row];
+  read_frags(0, av);
+  int64_t ct = w;
+  if constexpr (!kSample && !kShared) {
+    for (int i = 0; i + 1 < my_tiles; ++i) {
 #pragma unroll
-  for (int c = 0; c < kRChunks; ++c) step(c, kRChunks - 1 - c);
-  emit(ct);
+      for (int c = 0; c < kRChunks; ++c) step(c, kRChunks);
+      capture(ct);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) drain(e);
+      ct += G;
+    }
+#pragma unroll
+    for (int c = 0; c < kRChunks; ++c) step(c, kRChunks - 1 - c);
+    capture(ct);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) drain(e);
+  } else {
+    for (int i = 0; i + 1 < my_tiles; ++i) {
+#pragma unroll
+      for (int c = 0; c < kRChunks; ++c) step(c, kRChunks);
+      emit(ct);
+      ct += G;
+    }
+#pragma unroll
+    for (int c = 0; c < kRChunks; ++c) step(c, kRChunks - 1 - c);
+    emit(ct);
+  }
   wait_vm<0>();
   if (!kSample) {
-    if (grp == 0 && q_ok) a.count[(int64_t)q * kTopkMaxScanWG + w] = q_count;
+    if (kShared) {
+      __syncthreads();   // every wave's positions are taken
+      if (tid < 32 && tid < a.n_q) a.count[(int64_t)tid * kTopkMaxScanWG + w] = sm.qcount[tid];
+    } else if (grp == 0 && q_ok) {
+      a.count[(int64_t)q * kTopkMaxScanWG + w] = q_count;
+    }
     // the wave's own staged entries (written by this wave only)
     const uint32_t used = !stage_ok ? 0u : staged < (uint32_t)kCandWave ? staged : (uint32_t)kCandWave;
     for (uint32_t i = lane; i < used; i += 64) {
@@ -671,11 +843,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
       for (int64_t i = tid; i < n; i += kSelThreads) fn(src[i]);
     }, n, a.k, sh);
   }
-  if (tid == 0) {
-    // code 0 marks an empty group: fewer than k groups reached the bound
-    const float t = kth == 0 ? -INFINITY : float_of(kth);
-    a.tau[q] = kth == 0 ? t : t - (fabsf(t) * 0x1p-20f + 0x1p-100f);
-  }
+  if (tid == 0) a.tau[q] = tau_of_code(kth);
 }
 
 // Per query: the k best candidates, in order.
@@ -813,9 +981,12 @@ hipError_t launch_emb_compact(const uint16_t* from, const int32_t* keep, int64_t
   return hipGetLastError();
 }
 
+// A sample of S facts leaves about k * N / S candidates per query.  The
+// sample scan costs about one tile per workgroup whatever S is, up to a tile
+// for every CU, so small stores take 8192 facts (256 tiles of 32).
 int64_t topk_sample_size(int64_t n_facts) {
   int64_t s = n_facts / 32;
-  if (s < 4096) s = 4096;
+  if (s < 8192) s = 8192;
   s = (s + kFT - 1) / kFT * kFT;
   return s < n_facts ? s : n_facts;
 }
@@ -847,19 +1018,24 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
     return hipErrorInvalidValue;
   TopkLaunch a = in;
   const int32_t padded = topk_padded_dim(a.emb_dim);
-  // query tiles of 32 the launch fills: 1, 2 or 4.  Full batches at width
-  // 1024 keep their queries in registers: the stream in 128-fact tiles from
-  // 131,072 facts on, in 32-fact tiles below (every workgroup busy), the
-  // sample in the largest tile that still gives it IS_TOPK_SAMPLE_WGS
-  // workgroups.  Other batches and widths use the staged scan for both.
+  // query tiles of 32 the launch fills: 1, 2 or 4.  At width 1024, full
+  // batches keep their queries in registers: the stream in 128-fact tiles
+  // from 131,072 facts on, in 32-fact tiles below (every workgroup busy),
+  // the sample in the largest tile that still gives it IS_TOPK_SAMPLE_WGS
+  // workgroups.  Batches of at most 32 queries share one query tile across
+  // the waves (128-fact tiles).  Other batches and widths use the staged scan.
   const int qt = a.n_q <= 32 ? 1 : a.n_q <= 64 ? 2 : 4;
-  const bool resident = IS_TOPK_RESIDENT && qt == 4 && padded == kRChunks * kKC;
+  const bool wide = IS_TOPK_RESIDENT && padded == kRChunks * kKC;
+  const bool resident = wide && qt == 4;
+  const bool shared = wide && qt == 1;
   a.sample_n = topk_sample_size(a.n_facts);
   int ft_stream = kFT, ft_sample = kFT;
-  if (resident) {
-    ft_stream = a.n_facts >= kResidentBigFacts ? 128 : 32;
+  if (shared) {
+    ft_stream = ft_sample = 128;
+  } else if (resident) {
+    ft_stream = a.n_facts >= kResidentBigFacts ? IS_TOPK_BIG_STREAM_FT : IS_TOPK_SMALL_STREAM_FT;
     ft_sample = 32;
-    for (int f : {128, 64})
+    for (int f : {64})
       if ((a.sample_n + f - 1) / f >= IS_TOPK_SAMPLE_WGS) {
         ft_sample = f;
         break;
@@ -883,14 +1059,16 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
   auto scan = [&](bool sample, unsigned wgs) {
     const dim3 g(wgs), b(kThreads);
     const int ft = sample ? ft_sample : ft_stream;
-    if (resident) {
+    if (shared) {
+      if (sample) hipLaunchKernelGGL((topk_scan_rq<true, 128, true>), g, b, 0, stream, a);
+      else hipLaunchKernelGGL((topk_scan_rq<false, 128, true>), g, b, 0, stream, a);
+    } else if (resident) {
       if (sample) {
-        if (ft == 128) hipLaunchKernelGGL((topk_scan_rq<true, 128>), g, b, 0, stream, a);
-        else if (ft == 64) hipLaunchKernelGGL((topk_scan_rq<true, 64>), g, b, 0, stream, a);
-        else hipLaunchKernelGGL((topk_scan_rq<true, 32>), g, b, 0, stream, a);
+        if (ft == 64) hipLaunchKernelGGL((topk_scan_rq<true, 64, false>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((topk_scan_rq<true, 32, false>), g, b, 0, stream, a);
       } else {
-        if (ft == 128) hipLaunchKernelGGL((topk_scan_rq<false, 128>), g, b, 0, stream, a);
-        else hipLaunchKernelGGL((topk_scan_rq<false, 32>), g, b, 0, stream, a);
+        if (ft == 64) hipLaunchKernelGGL((topk_scan_rq<false, 64, false>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((topk_scan_rq<false, 32, false>), g, b, 0, stream, a);
       }
     } else if (sample) {
       if (qt == 1) hipLaunchKernelGGL((topk_scan<true, 1>), g, b, 0, stream, a);
@@ -902,8 +1080,11 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
       else hipLaunchKernelGGL((topk_scan<false, 4>), g, b, 0, stream, a);
     }
   };
+  // at most four queries on the shared tile: the stream finds the bounds
+  a.fuse_tau = shared && a.n_q <= kWaves && a.n_groups <= kWaveKthMax;
   scan(true, (unsigned)sample_wgs);
-  hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
+  if (!a.fuse_tau)
+    hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
   scan(false, (unsigned)a.scan_wgs);
   hipLaunchKernelGGL(topk_final, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();

@@ -246,6 +246,15 @@ def test_inject_invalid_call_writes_nothing(gpu):
                              # by the staged scan; k at its maximum
     (131100, 992, 70, 9),    # width 992: queries padded to 1024 through the scratch
                              # copy, then held in registers
+    (50000, 1024, 1, 5),     # one request on the Mistral-shaped index: the query tile
+                             # shared by the four waves, 391 tiles of 128
+    (9001, 1024, 32, 64),    # shared query tile, every row valid, k at its maximum
+    (300, 1024, 5, 7),       # shared query tile, three tiles (the sample is the store)
+    (100, 1024, 3, 64),      # bound found inside the stream scan; fewer sample groups
+                             # than k, so the bound is -inf and every fact is a candidate
+    (20000, 1024, 4, 64),    # bound inside the stream scan, one query per wave
+    (600000, 1024, 1, 9),    # shared query tile over a sample of 1,176 groups: the
+                             # separate threshold kernel
 ])
 def test_topk_parity(gpu, n_facts, dim, n_q, k):
     w = W.WORKLOADS["tiny"].scaled(name="topk", n_facts=n_facts, emb_dim=dim, n_req=n_q,
@@ -282,12 +291,14 @@ def test_topk_ties_and_self_match(gpu):
         st.destroy()
 
 
-def test_topk_many_candidates_full_batch(gpu):
+@pytest.mark.parametrize("n_q", [100, 20])
+def test_topk_many_candidates_full_batch(gpu, n_q):
     """A store where almost every fact shares one embedding: every fact of a
     workgroup's tiles reaches the sample bound, so candidates overflow the
     scan's staging area and the final selection gathers from the full list.
-    Equal scores go to the lower ids."""
-    w = W.WORKLOADS["tiny"].scaled(name="flat1024", n_facts=140001, emb_dim=1024, n_req=100,
+    Equal scores go to the lower ids.  100 queries: one query tile per wave;
+    20: one tile shared by the waves, positions from the workgroup's counter."""
+    w = W.WORKLOADS["tiny"].scaled(name="flat1024", n_facts=140001, emb_dim=1024, n_req=n_q,
                                    len_dist=("uniform", 1, 1))
     lens = W.fact_lengths(w)
     emb = W.fact_embeddings(w)
@@ -302,7 +313,7 @@ def test_topk_many_candidates_full_batch(gpu):
     try:
         q = W.query_embeddings(w)
         ids, sc = Hn.gpu_topk(st, q, 10)
-        Hn.check_topk(q, st.emb, ids, sc, 10, queries=range(0, 100, 9))
+        Hn.check_topk(q, st.emb, ids, sc, 10, queries=range(0, n_q, 9))
         for r in range(q.shape[0]):
             shared = [int(f) for f in ids[r] if f not in distinct]
             # facts of the shared embedding come in id order, the lowest first
