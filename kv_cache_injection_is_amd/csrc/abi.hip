@@ -716,9 +716,11 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   // batches of more than one request are grouped by fact id on the device
   const bool sort = n_req > 1;
   const size_t off_tmp = off_work + align256((size_t)n_items * sizeof(is::WorkItem));
-  const size_t off_buckets = off_tmp + (sort ? align256((size_t)n_items * sizeof(is::WorkItem)) : 0);
-  const size_t off_g = off_buckets + (sort ? align256(2 * is::kComposeBuckets * sizeof(uint32_t)) : 0);
-  const size_t off_bits = off_g + align256((size_t)n_pairs * 8);
+  const size_t off_g = off_tmp + (sort ? align256((size_t)n_items * sizeof(is::WorkItem)) : 0);
+  // the bucket counters and the slot bitmap are contiguous: the first top-k
+  // launch's sample scan zeroes them in one range
+  const size_t off_buckets = off_g + align256((size_t)n_pairs * 8);
+  const size_t off_bits = off_buckets + (sort ? align256(2 * is::kComposeBuckets * sizeof(uint32_t)) : 0);
   const size_t total = off_bits + align256((size_t)slot_words * 8);
   // Under stream capture: the graph workspace, no events, no allocation.
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
@@ -749,8 +751,13 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   int32_t* ids = ids_out ? ids_out : reinterpret_cast<int32_t*>(p + off_ids);
   float* scores = reinterpret_cast<float*>(p + off_scores);
   for (int32_t q0 = 0; q0 < n_req; q0 += 128) {
-    const is::TopkLaunch a =
+    is::TopkLaunch a =
         topk_launch_of(s, q, q0, std::min<int32_t>(128, n_req - q0), k, p, lay, ids, scores);
+    if (q0 == 0) {
+      a.zero = reinterpret_cast<uint32_t*>(p + off_buckets);
+      a.zero_words = (int64_t)((total - off_buckets) / 4);
+      a.zero_status = status;
+    }
     if ((e = is::launch_topk(a, st)) != hipSuccess) return hip_fail(e, "top-k launch");
   }
   is::ComposeLaunch c{};
@@ -775,6 +782,7 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   c.g_out = reinterpret_cast<float2*>(p + off_g);
   c.status = status;
   c.n_pairs = n_pairs;
+  c.cleared = n_req > 0;
   for (int32_t i = 0; i < n_pairs; ++i) c.g[i] = make_float2(g[2 * i], g[2 * i + 1]);
   if ((e = is::launch_compose(c, st)) != hipSuccess) return hip_fail(e, "compose launch");
   is::InjectLaunch a{};

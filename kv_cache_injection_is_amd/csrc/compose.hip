@@ -10,9 +10,11 @@
 // (the smallest code wins, so the result does not depend on timing) and the
 // inject kernel then writes nothing.
 //
-// Kernels: a clear (status and the slot bitmap to zero, rotation speeds
-// to their device buffer); the composer, one wave per request (k <= 64,
-// one selected fact per lane): an inclusive scan of the lengths gives the
+// Kernels: a clear (status, counters and the slot bitmap to zero; a
+// retrieve-and-inject call has its top-k sample scan do it instead); the
+// composer, one wave per request (k <= 64, one selected fact per lane; the
+// first also copies the rotation speeds to their device buffer): an
+// inclusive scan of the lengths gives the
 // positions, and each lane marks its share of the request's block runs in
 // the bitmap with 64-bit atomic ORs -- a bit that was already set is a slot
 // used twice; and, for batches, a counting sort of the list into 4096
@@ -36,7 +38,6 @@ __global__ __launch_bounds__(kClearThreads) void compose_clear(ComposeLaunch a) 
   for (int64_t i = i0; i < a.slot_words; i += stride) a.slot_bits[i] = 0;
   if (a.work_tmp != nullptr)
     for (int64_t i = i0; i < 2 * kComposeBuckets; i += stride) a.buckets[i] = 0;
-  if (i0 < a.n_pairs) a.g_out[i0] = a.g[i0];
   if (i0 == 0) *a.status = IS_OK;
 }
 
@@ -67,6 +68,8 @@ __device__ bool mark(uint64_t* bits, int64_t b0, int64_t b1) {
 __global__ __launch_bounds__(64) void compose(ComposeLaunch a) {
   const int r = blockIdx.x;
   const int lane = threadIdx.x;
+  if (r == 0)
+    for (int i = lane; i < a.n_pairs; i += 64) a.g_out[i] = a.g[i];
   const bool mine = lane < a.k;
   const int32_t f = mine ? a.ids[(int64_t)r * a.k + lane] : 0;
   const bool id_ok = f >= 0 && (int64_t)f < a.n_facts;
@@ -172,7 +175,8 @@ hipError_t launch_compose(const ComposeLaunch& a, hipStream_t stream) {
   int64_t blocks = (a.slot_words + kClearThreads - 1) / kClearThreads;
   if (blocks < 1) blocks = 1;
   if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(compose_clear, dim3((unsigned)blocks), dim3(kClearThreads), 0, stream, a);
+  if (!a.cleared || a.n_req == 0)
+    hipLaunchKernelGGL(compose_clear, dim3((unsigned)blocks), dim3(kClearThreads), 0, stream, a);
   if (a.n_req > 0) {
     hipLaunchKernelGGL(compose, dim3((unsigned)a.n_req), dim3(64), 0, stream, a);
     if (a.work_tmp != nullptr) {

@@ -54,10 +54,13 @@ struct ComposeLaunch {
   float2* g_out;            // [n_pairs] out: the rotation speeds, copied from `g`
   int32_t* status;          // out: IS_OK or an error code
   int32_t n_pairs;
+  int32_t cleared;          // the bitmap, buckets and status are zero already (the
+                            // top-k sample scan of the same call cleared them)
   float2 g[kComposeMaxPairs];
 };
 
-// Clears the bitmap and status, then composes and validates every request.
+// Clears the bitmap and status (unless `cleared`), then composes and
+// validates every request.
 hipError_t launch_compose(const ComposeLaunch& a, hipStream_t stream);
 
 // Query-only attention over the paged cache (bf16, head_dim 128).
@@ -130,6 +133,12 @@ struct TopkLaunch {
   uint64_t* cand;         // [n_q][cand_stride] candidate (score, id) keys
   int32_t* ids;           // [n_q][k]
   float* scores;          // [n_q][k]
+  // optional side job of the sample scan: words [zero, zero + zero_words)
+  // and *zero_status are set to 0 (a retrieve-and-inject call's composition
+  // counters, slot bitmap and status)
+  uint32_t* zero;
+  int64_t zero_words;
+  int32_t* zero_status;
 };
 
 // Scatters rows [first, first + n) given row-major (emb_dim wide) in device

@@ -110,28 +110,63 @@ __device__ __forceinline__ float tau_of_code(uint32_t kth) {
   return kth == 0 ? t : t - (fabsf(t) * 0x1p-20f + 0x1p-100f);
 }
 
-// The k-th largest of the n (<= 1024) order codes at src, by one wave: bit
-// by bit from the top, a bit is kept when at least k codes reach the prefix
-// with it set, which ends at the largest x that k codes reach.  0 when
-// fewer than k codes are nonzero.
+// A lower bound on the k-th largest of n (<= 1024) order codes held by a
+// wave, code lane + 64 j in v[j] (0 past n), exact to 20 bits below the
+// prefix that all nonzero codes share: the search starts from that common
+// prefix and keeps a bit when at least k codes reach the prefix with it
+// set.  Any code that k codes reach is a valid bound, and the low bits it
+// gives up only let a few more facts through as candidates.  0 when fewer
+// than k codes are nonzero.
 constexpr int kWaveKthMax = 1024;
-__device__ uint32_t wave_kth_code(const uint32_t* __restrict__ src, int64_t n, int k) {
+__device__ __forceinline__ void wave_load_codes(const uint32_t* __restrict__ src, int64_t n,
+                                                uint32_t (&v)[kWaveKthMax / 64]) {
   const int lane = threadIdx.x & 63;
-  const int slots = (int)((n + 63) / 64);
-  uint32_t v[kWaveKthMax / 64];
 #pragma unroll
   for (int j = 0; j < kWaveKthMax / 64; ++j)
-    v[j] = (j < slots && lane + 64 * j < n) ? src[lane + 64 * j] : 0u;
-  uint32_t prefix = 0;
-  for (int b = 31; b >= 0; --b) {
+    v[j] = (lane + 64 * j < n) ? src[lane + 64 * j] : 0u;
+}
+template <int S>
+__device__ uint32_t wave_kth_code_s(const uint32_t (&v)[kWaveKthMax / 64], int k) {
+  uint32_t hi = 0, lo = 0xFFFFFFFFu, nz = 0;
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    hi = v[j] > hi ? v[j] : hi;
+    lo = (v[j] != 0u && v[j] < lo) ? v[j] : lo;
+    nz += (uint32_t)__builtin_popcountll(__ballot(v[j] != 0u));
+  }
+  if (nz < (uint32_t)k) return 0u;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t h = (uint32_t)__shfl_xor((int)hi, off), l = (uint32_t)__shfl_xor((int)lo, off);
+    hi = h > hi ? h : hi;
+    lo = l < lo ? l : lo;
+  }
+  const int common = __builtin_clz(hi ^ lo | 1u);   // leading bits every nonzero code shares
+  const int top = 31 - common;                       // highest bit left to decide
+  uint32_t prefix = common == 0 ? 0u : (hi & ~(0xFFFFFFFFu >> common));
+  const int last = top - 19 > 0 ? top - 19 : 0;
+  for (int b = top; b >= last; --b) {
     const uint32_t cand = prefix | (1u << b);
     uint32_t cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kWaveKthMax / 64; ++j)
-      if (j < slots) cnt += (uint32_t)__builtin_popcountll(__ballot(v[j] >= cand));
+    for (int j = 0; j < S; ++j) cnt += (uint32_t)__builtin_popcountll(__ballot(v[j] >= cand));
     if (cnt >= (uint32_t)k) prefix = cand;
   }
   return prefix;
+}
+__device__ uint32_t wave_kth_code(const uint32_t (&v)[kWaveKthMax / 64], int64_t n, int k) {
+  return n <= 512 ? wave_kth_code_s<8>(v, k) : wave_kth_code_s<16>(v, k);
+}
+
+// Side job of the sample scan (a retrieve-and-inject call): zero the words
+// the composition of the same call counts and marks in, and its status
+// word, so that no separate clearing launch sits on the request's path; the
+// launches in between order them.
+__device__ __forceinline__ void side_zero(const TopkLaunch& a) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.zero_words; i += stride)
+    a.zero[i] = 0u;
+  if (a.zero_status != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.zero_status = 0;
 }
 
 // First tile of workgroup w when n_tiles tiles are dealt round-robin to G
@@ -243,6 +278,7 @@ template <bool kSample, int QT>
 __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
   constexpr int kQDma = q_dma<QT>();
   __shared__ ScanSmem sm;
+  if (kSample) side_zero(a);
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
@@ -485,6 +521,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   static_assert(!kShared || R::kRows == kWaves, "shared queries: one row tile per wave");
   constexpr int kRowsW = kShared ? 1 : R::kRows;   // row tiles a wave scores per stage
   __shared__ ScanSmemRq<FT> sm;
+  if (kSample) side_zero(a);
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
@@ -510,6 +547,10 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
     if (tid < 32) sm.qcount[tid] = 0;
     __syncthreads();
   }
+  // fuse: wave w's query's sample group maxima, loaded ahead of the ring so
+  // that waiting for them does not wait for the ring's transfers
+  uint32_t gv[kWaveKthMax / 64];
+  if (fuse && wave < a.n_q) wave_load_codes(a.gmax + (int64_t)wave * a.n_groups, a.n_groups, gv);
   half8 qv[kRChunks * 4];   // this lane's query row, loaded after the ring prologue
 
   const uint32_t e_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.e[0][0];
@@ -592,11 +633,11 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
 
   // Batch stream epilogue.  Candidates are rare (a few per 32 x 32 row
   // tile), so the wave takes one ballot per fragment element: an element no
-  // lane keeps costs a compare and a scalar branch, a kept one a few
-  // instructions.  `capture` keeps a tile's scores (padding masked) and
-  // notes which row tiles hold any candidate; `drain(e)` takes element e of
-  // those row tiles.  A query's two lanes see each other's bit in the
-  // ballot, which orders their candidates (the grp 0 lane's first).
+  // lane keeps costs a compare, a kept one a few instructions.  `capture`
+  // keeps a tile's scores (padding masked) and notes which row tiles hold
+  // any candidate; `drain_all` appends their candidates.  A query's two
+  // lanes see each other's bit in the ballot, which orders their candidates
+  // (the grp 0 lane's first).
   float dv[kRowsW][16];   // scores of the captured tile
   int64_t d_t = 0;        // the captured tile
   uint32_t d_any = 0;     // bit fw: row tile fw of the captured tile has candidates
@@ -614,30 +655,39 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
       if (__any(q_ok && mx >= tau)) d_any |= 1u << fw;
     }
   };
-  auto drain = [&](int e) {
+  // Every element's ballot first (no branches), then a scalar loop over
+  // the elements some lane keeps, reading the score at a uniform index.
+  auto drain_all = [&]() {
 #pragma unroll
     for (int fw = 0; fw < kRowsW; ++fw) {
       if (!(d_any & (1u << fw))) continue;   // uniform
-      const bool hit = q_ok && dv[fw][e] >= tau;
-      const uint64_t bal = __ballot(hit);
-      if (bal == 0) continue;
-      const uint32_t b_pair = (uint32_t)(bal >> (lane ^ 32)) & 1u;
-      const uint32_t pos = q_count + (grp ? b_pair : 0u);
-      q_count += (uint32_t)hit + b_pair;
-      if (hit) {
-        const uint32_t slot = staged + __builtin_amdgcn_mbcnt_hi(
-                                           (uint32_t)(bal >> 32),
-                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        const uint32_t f = (uint32_t)(d_t * FT) + fw * 32 + 4 * grp + 8 * (e / 4) + (e % 4);
-        const uint64_t key = key_of(ord_of(dv[fw][e]), f);
-        if (stage_ok && slot < (uint32_t)kCandWave) {
-          sm.ckey[wave][slot] = key;
-          sm.cdst[wave][slot] = ((uint32_t)q << kPosBits) | pos;
-        } else {
-          a.cand[(int64_t)q * a.cand_stride + region0 + pos] = key;
+      uint32_t act = 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) act |= __ballot(q_ok && dv[fw][e] >= tau) != 0 ? 1u << e : 0u;
+      while (act != 0) {
+        const int e = __builtin_ctz(act);
+        act &= act - 1;
+        const float x = dv[fw][e];
+        const bool hit = q_ok && x >= tau;
+        const uint64_t bal = __ballot(hit);
+        const uint32_t b_pair = (uint32_t)(bal >> (lane ^ 32)) & 1u;
+        const uint32_t pos = q_count + (grp ? b_pair : 0u);
+        q_count += (uint32_t)hit + b_pair;
+        if (hit) {
+          const uint32_t slot = staged + __builtin_amdgcn_mbcnt_hi(
+                                             (uint32_t)(bal >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          const uint32_t f = (uint32_t)(d_t * FT) + fw * 32 + 4 * grp + 8 * (e >> 2) + (e & 3);
+          const uint64_t key = key_of(ord_of(x), f);
+          if (stage_ok && slot < (uint32_t)kCandWave) {
+            sm.ckey[wave][slot] = key;
+            sm.cdst[wave][slot] = ((uint32_t)q << kPosBits) | pos;
+          } else {
+            a.cand[(int64_t)q * a.cand_stride + region0 + pos] = key;
+          }
         }
+        staged += (uint32_t)__builtin_popcountll(bal);
       }
-      staged += (uint32_t)__builtin_popcountll(bal);
     }
   };
 
@@ -707,8 +757,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
     if (fuse) {
       // while the ring's first stages land: wave w finds query w's bound
       if (wave < a.n_q) {
-        const float t = tau_of_code(
-            wave_kth_code(a.gmax + (int64_t)wave * a.n_groups, a.n_groups, a.k));
+        const float t = tau_of_code(wave_kth_code(gv, a.n_groups, a.k));
         if (lane == 0) sm.qtau[wave] = t;
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the bound is in LDS before the barrier
@@ -725,15 +774,13 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
 #pragma unroll
       for (int c = 0; c < kRChunks; ++c) step(c, kRChunks);
       capture(ct);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) drain(e);
+      drain_all();
       ct += G;
     }
 #pragma unroll
     for (int c = 0; c < kRChunks; ++c) step(c, kRChunks - 1 - c);
     capture(ct);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) drain(e);
+    drain_all();
   } else {
     for (int i = 0; i + 1 < my_tiles; ++i) {
 #pragma unroll
@@ -893,6 +940,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
         if (i0 + j < cnt) keys[excl + i0 + j] = t[j];
     }
     __syncthreads();
+    if (total <= 64) {
+      // few candidates (one request, small k): one wave sorts them all
+      if (tid < 64) {
+        const uint64_t v = wave_sort_desc(tid < (int)total ? keys[tid] : 0ull);
+        if (tid < a.k) {
+          a.ids[(int64_t)q * a.k + tid] = v ? (int32_t)(0xFFFFFFFFu - (uint32_t)v) : -1;
+          a.scores[(int64_t)q * a.k + tid] = v ? float_of((uint32_t)(v >> 32)) : -INFINITY;
+        }
+      }
+      return;
+    }
     const uint64_t thr = kth_largest<uint64_t>([&](auto fn) {
       for (uint32_t i = tid; i < total; i += kSelThreads) fn(keys[i]);
     }, total, a.k, sh);
