@@ -72,6 +72,9 @@
 #ifndef IS_R16_LAYER_FAST
 #define IS_R16_LAYER_FAST 1     // grid x = layer group (consecutive workgroups share a fact)
 #endif
+#ifndef IS_R16_ONE_PER_CU
+#define IS_R16_ONE_PER_CU 65536 // dynamic LDS (bytes) requested by the long-fact launch so that
+#endif                          // one 512-lane workgroup runs per CU (0: as many as fit)
 #ifndef IS_R16_HOST_WHOLE
 #define IS_R16_HOST_WHOLE 1     // one workgroup moves all layers of a host-tier fact
 #endif
@@ -301,34 +304,42 @@ __global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
       const int64_t base = (int64_t)l0 * H * len * D * ES;
       const char* __restrict__ ksrc = reinterpret_cast<const char*>(w.k) + base;
       const char* __restrict__ vsrc = reinterpret_cast<const char*>(w.v) + base;
+      // r -> (layer g, head h, token t); exact for r < 2^16
+      auto split_row = [&](int r, int& g, int& h, int& t) {
+        g = (int)(((float)r + 0.5f) * inv_pl);
+        const int rem = r - g * per_layer;
+        h = (int)(((float)rem + 0.5f) * inv_tc);
+        t = rem - h * tc;
+      };
       for (int r0 = tid / 16; r0 < rows; r0 += U * RPS) {
         u32x4 kv[U], vv[U];
-        int gl[U], hh[U], tt[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int r = r0 + u * RPS;
-          // r -> (layer g, head h, token t); exact for r < 2^16
-          const int g = (int)(((float)r + 0.5f) * inv_pl);
-          const int rem = r - g * per_layer;
-          const int h = (int)(((float)rem + 0.5f) * inv_tc);
-          gl[u] = g;
-          hh[u] = h;
-          tt[u] = rem - h * tc;
+          int g, h, t;
+          split_row(r, g, h, t);
           if (r < rows) {
-            const int64_t e = ((int64_t)(g * H + h) * len + t0 + tt[u]) * D + col;
+            const int64_t e = ((int64_t)(g * H + h) * len + t0 + t) * D + col;
             kv[u] = load16(ksrc + e * ES);
             vv[u] = load16(vsrc + e * ES);
           }
         }
+        // The row's (layer, head, token) again for the stores, from an
+        // opaque copy of the row index: kept from the loads, they would hold
+        // 3 U registers across the wait (133 registers in all instead of 110).
+        int r0s;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(r0s) : "v"(r0));
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int r = r0 + u * RPS;
+          const int r = r0s + u * RPS;
+          int gl_u, hh_u, tt_u;
+          split_row(r, gl_u, hh_u, tt_u);
           if (r < rows) {   // uniform across each 16-lane row
             u32x4 other;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               other[q] = (unsigned)__builtin_amdgcn_mov_dpp((int)kv[u][q], 0x128, 0xF, 0xF, false);
-            const float2* csr = cs + tt[u] * HALF + fcol;
+            const float2* csr = cs + tt_u * HALF + fcol;
             u32x4 out;
             if constexpr (ES == 4) {
 #pragma unroll
@@ -350,8 +361,8 @@ __global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
                 out[q] = pack_bf16(y0, y1);
               }
             }
-            const int64_t dst = (int64_t)(l0 + gl[u]) * a.s_layer + slot_off[tt[u]] +
-                                (int64_t)hh[u] * a.s_head + col;
+            const int64_t dst = (int64_t)(l0 + gl_u) * a.s_layer + slot_off[tt_u] +
+                                (int64_t)hh_u * a.s_head + col;
             store16(kc + dst * ES, out);
             store16(vc + dst * ES, vv[u]);
           }
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(T) void inject_row16(InjectLaunch a) {
 }
 
 template <int ES, int T, int U>
-hipError_t launch_r16(const InjectLaunch& a, hipStream_t stream) {
+hipError_t launch_r16(const InjectLaunch& a, hipStream_t stream, size_t pad_lds) {
   const unsigned n_groups = (unsigned)((a.n_layers + a.layers_per_wg - 1) / a.layers_per_wg);
   // the item index is grid y: launch at most 65535 items at a time
   constexpr int32_t kMaxItems = IS_R16_LAYER_FAST ? 65535 : INT32_MAX;
@@ -373,7 +384,7 @@ hipError_t launch_r16(const InjectLaunch& a, hipStream_t stream) {
     part.n_items = a.n_items - i0 < kMaxItems ? a.n_items - i0 : kMaxItems;
     const dim3 grid16 = IS_R16_LAYER_FAST ? dim3(n_groups, (unsigned)part.n_items)
                                           : dim3((unsigned)part.n_items, n_groups);
-    hipLaunchKernelGGL((inject_row16<ES, T, U, IS_R16_TC>), grid16, dim3(T), 0, stream, part);
+    hipLaunchKernelGGL((inject_row16<ES, T, U, IS_R16_TC>), grid16, dim3(T), pad_lds, stream, part);
   }
   return hipGetLastError();
 }
@@ -392,8 +403,13 @@ hipError_t launch_es(const InjectLaunch& in, hipStream_t stream) {
     int g = short_facts ? (int)((float)IS_R16_SHORT_ROWS / rows + 0.999f) : 1;
     if (IS_R16_FIXED_LAYERS > 0) g = IS_R16_FIXED_LAYERS;
     a.layers_per_wg = g < a.n_layers ? g : a.n_layers;
-    return short_facts ? launch_r16<ES, IS_R16_SHORT_THREADS, IS_R16_SHORT_U>(a, stream)
-                       : launch_r16<ES, IS_R16_THREADS, IS_R16_ROWS>(a, stream);
+    // Long facts: one workgroup per CU.  With two (their registers allow
+    // it), the Mistral-shaped batch measured 1.5% slower (more concurrent
+    // DRAM streams against the memory system's mixed read/write limit) and
+    // the Llama-3.1 Zipf batch, whose repeated facts hit the cache, 11%
+    // faster; the batch the step is quoted on decides.
+    return short_facts ? launch_r16<ES, IS_R16_SHORT_THREADS, IS_R16_SHORT_U>(a, stream, 0)
+                       : launch_r16<ES, IS_R16_THREADS, IS_R16_ROWS>(a, stream, IS_R16_ONE_PER_CU);
   }
   const dim3 grid((unsigned)in.n_items, (unsigned)in.n_layers);
   switch (in.lanes) {

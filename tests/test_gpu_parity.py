@@ -291,13 +291,14 @@ def test_topk_ties_and_self_match(gpu):
         st.destroy()
 
 
-@pytest.mark.parametrize("n_q", [100, 20])
+@pytest.mark.parametrize("n_q", [100, 20, 3])
 def test_topk_many_candidates_full_batch(gpu, n_q):
     """A store where almost every fact shares one embedding: every fact of a
     workgroup's tiles reaches the sample bound, so candidates overflow the
     scan's staging area and the final selection gathers from the full list.
     Equal scores go to the lower ids.  100 queries: one query tile per wave;
-    20: one tile shared by the waves, positions from the workgroup's counter."""
+    20: one tile shared by the waves, positions from the workgroup's counter;
+    3: the same, with the bound found inside the stream scan."""
     w = W.WORKLOADS["tiny"].scaled(name="flat1024", n_facts=140001, emb_dim=1024, n_req=n_q,
                                    len_dist=("uniform", 1, 1))
     lens = W.fact_lengths(w)
