@@ -750,16 +750,6 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   char* p = static_cast<char*>(sl->dev);
   int32_t* ids = ids_out ? ids_out : reinterpret_cast<int32_t*>(p + off_ids);
   float* scores = reinterpret_cast<float*>(p + off_scores);
-  for (int32_t q0 = 0; q0 < n_req; q0 += 128) {
-    is::TopkLaunch a =
-        topk_launch_of(s, q, q0, std::min<int32_t>(128, n_req - q0), k, p, lay, ids, scores);
-    if (q0 == 0) {
-      a.zero = reinterpret_cast<uint32_t*>(p + off_buckets);
-      a.zero_words = (int64_t)((total - off_buckets) / 4);
-      a.zero_status = status;
-    }
-    if ((e = is::launch_topk(a, st)) != hipSuccess) return hip_fail(e, "top-k launch");
-  }
   is::ComposeLaunch c{};
   c.ids = ids;
   c.prefix = prefix_len;
@@ -784,7 +774,20 @@ IS_EXPORT int is_retrieve_inject(const is_store* cs, const uint16_t* q, int32_t 
   c.n_pairs = n_pairs;
   c.cleared = n_req > 0;
   for (int32_t i = 0; i < n_pairs; ++i) c.g[i] = make_float2(g[2 * i], g[2 * i + 1]);
-  if ((e = is::launch_compose(c, st)) != hipSuccess) return hip_fail(e, "compose launch");
+  // One request: the top-k final kernel composes it (no composer launch).
+  const bool fused = n_req == 1;
+  for (int32_t q0 = 0; q0 < n_req; q0 += 128) {
+    is::TopkLaunch a =
+        topk_launch_of(s, q, q0, std::min<int32_t>(128, n_req - q0), k, p, lay, ids, scores);
+    if (q0 == 0) {
+      a.zero = reinterpret_cast<uint32_t*>(p + off_buckets);
+      a.zero_words = (int64_t)((total - off_buckets) / 4);
+      a.zero_status = status;
+    }
+    if ((e = is::launch_topk(a, st, fused ? &c : nullptr)) != hipSuccess)
+      return hip_fail(e, "top-k launch");
+  }
+  if (!fused && (e = is::launch_compose(c, st)) != hipSuccess) return hip_fail(e, "compose launch");
   is::InjectLaunch a{};
   a.kc = cache->k_base;
   a.vc = cache->v_base;

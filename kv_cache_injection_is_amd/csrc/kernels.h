@@ -159,6 +159,10 @@ struct TopkScratch {
   size_t q_off, gmax_off, tau_off, count_off, cand_off, bytes;
 };
 TopkScratch topk_scratch(int64_t n_facts, int32_t n_q, int32_t emb_dim);
-hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+// `compose` (one query only): the final kernel also composes and validates
+// that request, as launch_compose would (its clearing already done by the
+// sample scan's side job).
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream,
+                       const ComposeLaunch* compose = nullptr);
 
 }  // namespace is

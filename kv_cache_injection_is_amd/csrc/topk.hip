@@ -44,6 +44,7 @@
 //                 every fact's score is the same MFMA chain in both.
 #include <hip/hip_runtime.h>
 
+#include "compose_request.h"
 #include "kernels.h"
 
 #ifndef IS_TOPK_RESIDENT
@@ -894,13 +895,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
 }
 
 // Per query: the k best candidates, in order.
-__global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
-  __shared__ uint64_t keys[kStage64];
-  __shared__ SelShared sh;
-  __shared__ uint32_t wtot[kSelThreads / 64];
-  __shared__ uint64_t best[kMaxK];
-  __shared__ uint32_t n_best;
-  const int q = blockIdx.x;
+struct FinalShared {
+  uint64_t keys[kStage64];
+  SelShared sh;
+  uint32_t wtot[kSelThreads / 64];
+  uint64_t best[kMaxK];
+  uint32_t n_best;
+};
+
+// Query q's final selection by the whole workgroup; query q's ids and
+// scores are written by the first wave's lanes 0 .. k-1.
+__device__ void final_query(const TopkLaunch& a, int q, FinalShared& fs) {
+  uint64_t* keys = fs.keys;
+  SelShared& sh = fs.sh;
+  uint32_t* wtot = fs.wtot;
+  uint64_t* best = fs.best;
+  uint32_t& n_best = fs.n_best;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.scan_wgs;
   // thread t gathers the region of scan workgroup t
@@ -971,6 +981,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
       a.scores[(int64_t)q * a.k + tid] = v ? float_of((uint32_t)(v >> 32)) : -INFINITY;
     }
   }
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
+  __shared__ FinalShared fs;
+  final_query(a, blockIdx.x, fs);
+}
+
+// One request (one query): its final selection, then its composition by
+// the wave that wrote the ids (its own stores, in program order), so the
+// composer's launch drops out of the request's path.
+__global__ __launch_bounds__(kSelThreads) void topk_final_compose(TopkLaunch a, ComposeLaunch c) {
+  __shared__ FinalShared fs;
+  final_query(a, 0, fs);
+  if (threadIdx.x < 64) compose_request(c, 0, threadIdx.x);
 }
 
 // Scatters embedding rows [first, first + n) (row-major, `emb_dim` wide, in
@@ -1069,7 +1093,7 @@ TopkScratch topk_scratch(int64_t n_facts, int32_t n_q, int32_t emb_dim) {
   return s;
 }
 
-hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
+hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLaunch* compose) {
   if (in.n_q == 0) return hipSuccess;
   if (in.k < 1 || in.k > kMaxK || in.k > in.n_facts || in.n_q > kQB || in.emb_dim <= 0 ||
       in.emb_dim % 8 != 0)
@@ -1144,7 +1168,10 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream) {
   if (!a.fuse_tau)
     hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
   scan(false, (unsigned)a.scan_wgs);
-  hipLaunchKernelGGL(topk_final, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
+  if (compose != nullptr && a.n_q == 1)
+    hipLaunchKernelGGL(topk_final_compose, dim3(1), dim3(kSelThreads), 0, stream, a, *compose);
+  else
+    hipLaunchKernelGGL(topk_final, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -104,6 +104,15 @@ def test_device_validation_writes_nothing(gpu):
         # a negative prefix
         status, _ = _device_call(st, w, q[:1], 4, np.array([-1]), bt[:1], cache)
         assert status == -1
+        # one request whose table names one block twice inside its segment:
+        # its own slots collide (a single request is composed by the top-k
+        # final kernel)
+        b0 = int(prefix[0]) // w.block_size
+        assert need - 1 > b0
+        dup = bt[:1].copy()
+        dup[0, b0 + 1] = dup[0, b0]
+        status, _ = _device_call(st, w, q[:1], 4, prefix[:1], dup, cache)
+        assert status == -4
         # one good request next to a failing one: still nothing is written
         mixed = bt[:2].copy()
         mixed[1, :] = mixed[0, :]
