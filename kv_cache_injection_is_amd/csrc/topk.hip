@@ -14,16 +14,20 @@
 //      16 scores it holds to their maximum, so the sample is cut into
 //      disjoint groups of 16 facts and each group reports its best score;
 //   2. threshold: per query, the k-th largest group maximum (radix select)
-//      is tau -- k groups, hence k distinct facts, reach it;
+//      is tau -- k groups, hence k distinct facts, reach it (for at most
+//      four queries on the shared query tile the stream scan finds it);
 //   3. scan (stream mode): MFMA scores of all facts; a score >= tau is a
 //      candidate, appended to the workgroup's own region of the query's
-//      candidate list (position from an LDS counter, so the HBM stream is
-//      never drained to wait for a global atomic);
+//      candidate list (position from LDS or from the query's own lanes, so
+//      the HBM stream is never drained to wait for a global atomic);
 //   4. final: per query, the candidate regions are gathered, the k-th
 //      largest (score, then lower id) key is found by radix select, and the
-//      k winners are sorted across a wave.
-// Both scan modes run the same instruction sequence per tile, so a sample
-// fact scores identically in both.
+//      k winners are sorted across a wave (at most 64 candidates: sorted
+//      directly).  For one request of a retrieve-and-inject call the final
+//      kernel then composes the request.
+// Every scan computes a fact's score as the same MFMA chain, so a sample
+// fact scores identically in the sample and the stream, whatever the
+// variant or tile size, and a query scores alike alone or in a batch.
 //
 // Scan layout.  The store keeps the embeddings tile-blocked (see kernels.h):
 // every 256-fact x 64-dim block is one contiguous 32 KB span.  Persistent
@@ -31,17 +35,20 @@
 // tiles' blocks from memory straight into an LDS ring with
 // global_load_lds_dwordx4 (no registers on the way); v_mfma_f32_32x32x16_f16
 // forms the scores with fp32 accumulation.  Two variants:
-//   topk_scan     each wave owns 64 facts of a 256-fact tile against every
-//                 query tile the launch fills; the query chunk is staged
-//                 with the fact block in a 3-stage ring, and a wave refills
-//                 its own fact rows without waiting for the other waves;
-//   topk_scan_rq  full batches at width 1024: each wave keeps its 32 query
-//                 rows in registers for the whole launch and scores every
-//                 fact of a 32-, 64- or 128-fact tile, the ring (8 or 16
-//                 stages, all but one in flight) holds fact rows only, and
-//                 candidates are staged in LDS until the loop ends (see
-//                 below).  Sample and stream may use different tile sizes:
-//                 every fact's score is the same MFMA chain in both.
+//   topk_scan     other widths and 33-64-query batches: each wave owns 64
+//                 facts of a 256-fact tile against every query tile the
+//                 launch fills; the query chunk is staged with the fact
+//                 block in a 3-stage ring, and a wave refills its own fact
+//                 rows without waiting for the other waves;
+//   topk_scan_rq  width 1024: each wave keeps 32 query rows in registers
+//                 for the whole launch and the ring (8 or 16 stages, all
+//                 but one in flight) holds fact rows only.  Full batches
+//                 (65-128 queries): wave w holds query tile w and scores
+//                 every fact of a 32- or 64-fact tile, candidates staged in
+//                 LDS until the loop ends.  Batches of at most 32 (shared
+//                 mode): every wave holds the same tile and scores its own
+//                 32-fact row tile of a 128-fact stage.  Sample and stream
+//                 may use different tile sizes.
 #include <hip/hip_runtime.h>
 
 #include "compose_request.h"
@@ -50,15 +57,11 @@
 #ifndef IS_TOPK_RESIDENT
 #define IS_TOPK_RESIDENT 1   // full batches at width 1024 keep their queries in registers
 #endif
-#ifndef IS_TOPK_SMALL_STREAM_FT
-#define IS_TOPK_SMALL_STREAM_FT 32   // stream tile (facts) of full batches below 131,072 facts
-#endif
-#ifndef IS_TOPK_BIG_STREAM_FT
-#define IS_TOPK_BIG_STREAM_FT 32     // ... and from 131,072 facts on
-#endif
-static_assert((IS_TOPK_SMALL_STREAM_FT == 32 || IS_TOPK_SMALL_STREAM_FT == 64) &&
-                  (IS_TOPK_BIG_STREAM_FT == 32 || IS_TOPK_BIG_STREAM_FT == 64),
-              "stream tiles of 32 or 64 facts (128-fact tiles spill the spread candidate test)");
+#ifndef IS_TOPK_STREAM_FT
+#define IS_TOPK_STREAM_FT 32   // stream tile (facts) of full batches: 32 or 64 (32 measured
+#endif                         // faster on the 50k and the 1M index)
+static_assert(IS_TOPK_STREAM_FT == 32 || IS_TOPK_STREAM_FT == 64,
+              "stream tiles of 32 or 64 facts (128-fact tiles spill with the fragment prefetch)");
 #ifndef IS_TOPK_SAMPLE_WGS
 #define IS_TOPK_SAMPLE_WGS 192   // workgroups the sample scan should at least fill
 #endif
@@ -455,9 +458,6 @@ struct Rq {
   static_assert(kDma >= 1 && (kStages - 2) * kDma < 64, "vmcnt range");
   static_assert(kFT % FT == 0, "a tile is a part of a stored 256-fact block");
 };
-// Stores at least this large stream in 128-fact tiles (four or more per
-// workgroup); smaller ones in 32-fact tiles, which keep every workgroup busy.
-constexpr int64_t kResidentBigFacts = (int64_t)4 * kTopkMaxScanWG * 128;   // 131,072
 static_assert(kQB == kWaves * 32, "one 32-query tile per wave");
 
 // Candidates found during the stream are staged in LDS and written out
@@ -1101,11 +1101,11 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
   TopkLaunch a = in;
   const int32_t padded = topk_padded_dim(a.emb_dim);
   // query tiles of 32 the launch fills: 1, 2 or 4.  At width 1024, full
-  // batches keep their queries in registers: the stream in 128-fact tiles
-  // from 131,072 facts on, in 32-fact tiles below (every workgroup busy),
-  // the sample in the largest tile that still gives it IS_TOPK_SAMPLE_WGS
-  // workgroups.  Batches of at most 32 queries share one query tile across
-  // the waves (128-fact tiles).  Other batches and widths use the staged scan.
+  // batches keep their queries in registers: the stream in 32-fact tiles,
+  // the sample in 64-fact tiles when that still gives it IS_TOPK_SAMPLE_WGS
+  // workgroups, else 32.  Batches of at most 32 queries share one query
+  // tile across the waves (128-fact tiles).  Other batches and widths use
+  // the staged scan.
   const int qt = a.n_q <= 32 ? 1 : a.n_q <= 64 ? 2 : 4;
   const bool wide = IS_TOPK_RESIDENT && padded == kRChunks * kKC;
   const bool resident = wide && qt == 4;
@@ -1115,7 +1115,7 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
   if (shared) {
     ft_stream = ft_sample = 128;
   } else if (resident) {
-    ft_stream = a.n_facts >= kResidentBigFacts ? IS_TOPK_BIG_STREAM_FT : IS_TOPK_SMALL_STREAM_FT;
+    ft_stream = IS_TOPK_STREAM_FT;
     ft_sample = 32;
     for (int f : {64})
       if ((a.sample_n + f - 1) / f >= IS_TOPK_SAMPLE_WGS) {
