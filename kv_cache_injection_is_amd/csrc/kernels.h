@@ -119,6 +119,7 @@ struct TopkLaunch {
   int32_t k;
   int32_t scan_wgs;       // derived by launch_topk
   int32_t fuse_tau;       // derived by launch_topk: the stream scan finds the bounds
+  int32_t dense;          // derived by launch_topk: one scan writes every score (below)
   // derived by launch_topk; n_tiles counts stream tiles of scan_tile facts
   // and sample_tiles sample tiles of sample_tile facts (256 for the staged
   // scan; 32, 64 or 128 for the variant that keeps the queries in registers)
@@ -131,6 +132,11 @@ struct TopkLaunch {
   float* tau;             // [n_q] bound on each query's k-th best score
   uint32_t* count;        // [n_q][kTopkMaxScanWG] candidates per scan workgroup
   uint64_t* cand;         // [n_q][cand_stride] candidate (score, id) keys
+  // dense: the scan writes every fact's order code, grouped as the group
+  // maxima are ([n_q][code_stride], in the cand buffer), and gmax holds the
+  // maxima of all n_groups groups (after the codes, same buffer)
+  uint32_t* codes;
+  int64_t code_stride;
   int32_t* ids;           // [n_q][k]
   float* scores;          // [n_q][k]
   // optional side job of the sample scan: words [zero, zero + zero_words)

@@ -25,6 +25,13 @@
 //      k winners are sorted across a wave (at most 64 candidates: sorted
 //      directly).  For one request of a retrieve-and-inject call the final
 //      kernel then composes the request.
+// Small stores take one pass instead (at most 8M scores for the launch and
+// 131,072 facts, width 1024): the scan writes every fact's score as an
+// order code together with every group's maximum, and the final kernel
+// takes the bound from all the groups -- the k-th largest of its threads'
+// best group maxima -- then gathers the codes that reach it from the
+// groups whose maximum does (about k groups).  No sample scan and no
+// threshold launch; the codes cost 4 bytes per (query, fact) of writes.
 // Every scan computes a fact's score as the same MFMA chain, so a sample
 // fact scores identically in the sample and the stream, whatever the
 // variant or tile size, and a query scores alike alone or in a batch.
@@ -65,6 +72,9 @@ static_assert(IS_TOPK_STREAM_FT == 32 || IS_TOPK_STREAM_FT == 64,
 #ifndef IS_TOPK_SAMPLE_WGS
 #define IS_TOPK_SAMPLE_WGS 192   // workgroups the sample scan should at least fill
 #endif
+#ifndef IS_TOPK_DENSE_CODES
+#define IS_TOPK_DENSE_CODES (1 << 23)   // most score codes (queries x facts) the one-pass
+#endif                                  // mode writes; 0 turns it off
 
 namespace is {
 namespace {
@@ -516,13 +526,14 @@ __device__ __forceinline__ void wait_stages(int n) {
 // query rows (rows past n_q are zero and load nothing) and scores its own
 // 32-fact row tile of each 128-fact stage, so one query's candidates come
 // from all four waves and take their positions from an LDS counter.
-template <bool kSample, int FT, bool kShared>
+template <bool kSample, int FT, bool kShared, bool kDense = false>
 __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   using R = Rq<FT>;
   static_assert(!kShared || R::kRows == kWaves, "shared queries: one row tile per wave");
+  static_assert(!(kSample && kDense), "the one-pass scan is a stream scan");
   constexpr int kRowsW = kShared ? 1 : R::kRows;   // row tiles a wave scores per stage
   __shared__ ScanSmemRq<FT> sm;
-  if (kSample) side_zero(a);
+  if (kSample || kDense) side_zero(a);
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
@@ -537,8 +548,8 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   const bool q_ok = q < a.n_q;
   // the bound: from the threshold kernel, or (fuse_tau: at most four
   // queries, shared query tile) found below by wave q from the sample
-  const bool fuse = kShared && !kSample && a.fuse_tau;
-  float tau = (!kSample && !fuse && q_ok) ? a.tau[q] : 0.f;
+  const bool fuse = kShared && !kSample && !kDense && a.fuse_tau;
+  float tau = (!kSample && !kDense && !fuse && q_ok) ? a.tau[q] : 0.f;
   const uint64_t region0 = (uint64_t)region_tile(w, n_tiles, G) * FT;
   const bool stage_ok = (int64_t)my_tiles * FT <= ((int64_t)1 << kPosBits);
   uint32_t q_count = 0;    // candidates of this lane's query so far (both its lanes)
@@ -593,10 +604,22 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
       float mx = v[0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
-      if (kSample) {
+      if (kSample || kDense) {
         if (q_ok) {
           const int64_t gi = (t * R::kRows + ft) * 2 + grp;
           a.gmax[(int64_t)q * a.n_groups + gi] = (mx == -INFINITY) ? 0u : ord_of(mx);
+          if (kDense) {
+            // the group's 16 codes, in fragment order (0: padding)
+            u32x4* dst = reinterpret_cast<u32x4*>(a.codes + (int64_t)q * a.code_stride + gi * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              u32x4 c;
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                c[i] = v[4 * j + i] == -INFINITY ? 0u : ord_of(v[4 * j + i]);
+              dst[j] = c;
+            }
+          }
         }
         continue;
       }
@@ -770,7 +793,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   if (fuse && q_ok) tau = sm.qtau[row];
   read_frags(0, av);
   int64_t ct = w;
-  if constexpr (!kSample && !kShared) {
+  if constexpr (!kSample && !kShared && !kDense) {
     for (int i = 0; i + 1 < my_tiles; ++i) {
 #pragma unroll
       for (int c = 0; c < kRChunks; ++c) step(c, kRChunks);
@@ -794,7 +817,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
     emit(ct);
   }
   wait_vm<0>();
-  if (!kSample) {
+  if (!kSample && !kDense) {
     if (kShared) {
       __syncthreads();   // every wave's positions are taken
       if (tid < 32 && tid < a.n_q) a.count[(int64_t)tid * kTopkMaxScanWG + w] = sm.qcount[tid];
@@ -814,6 +837,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
 constexpr int kSelThreads = 256;
 constexpr int kStage32 = 8192;   // group maxima staged in LDS by the threshold kernel
 constexpr int kStage64 = 4096;   // candidate keys staged in LDS by the final kernel
+constexpr int kDenseGroups = 32 * kSelThreads;   // group maxima the one-pass final holds
 
 struct SelShared {
   uint32_t hist[256];
@@ -896,24 +920,92 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
 
 // Per query: the k best candidates, in order.
 struct FinalShared {
-  uint64_t keys[kStage64];
+  union {
+    uint64_t keys[kStage64];   // candidate keys
+    uint32_t vals[kSelThreads];   // one-pass mode: each thread's largest group maximum
+  };
   SelShared sh;
   uint32_t wtot[kSelThreads / 64];
   uint64_t best[kMaxK];
   uint32_t n_best;
+  uint32_t n_cand;
 };
 
-// Query q's final selection by the whole workgroup; query q's ids and
-// scores are written by the first wave's lanes 0 .. k-1.
-__device__ void final_query(const TopkLaunch& a, int q, FinalShared& fs) {
+// Barrier over the workgroup's LDS accesses only: global loads in flight
+// (the one-pass final's prefetched codes) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The k best of `total` candidate keys, as query q's ids and scores (the
+// threads of the workgroup that hold them write them).  `staged`: the keys sit in
+// fs.keys[0, total); otherwise each(fn) hands fn every key this thread
+// owns, read from memory.  fs.best and fs.n_best are cleared, and a barrier
+// has passed since.
+template <typename Each>
+__device__ void select_best(const TopkLaunch& a, int q, FinalShared& fs, uint32_t total,
+                            bool staged, Each each) {
+  const int tid = threadIdx.x;
   uint64_t* keys = fs.keys;
-  SelShared& sh = fs.sh;
-  uint32_t* wtot = fs.wtot;
-  uint64_t* best = fs.best;
-  uint32_t& n_best = fs.n_best;
+  auto write = [&](uint64_t v) {
+    // key 0: fewer candidates than k (cannot happen for a consistent
+    // bound); reported as id -1, score -inf
+    if (tid < a.k) {
+      a.ids[(int64_t)q * a.k + tid] = v ? (int32_t)(0xFFFFFFFFu - (uint32_t)v) : -1;
+      a.scores[(int64_t)q * a.k + tid] = v ? float_of((uint32_t)(v >> 32)) : -INFINITY;
+    }
+  };
+  if (staged && total <= 2 * kSelThreads) {
+    // a few hundred at most: every key counts the keys above it (the keys
+    // are distinct, so the counts are the final positions); positions past
+    // the candidates (fewer than k: cannot happen for a consistent bound)
+    // are reported as id -1, score -inf
+    // keys [total, total rounded up to 8) are zero, which ranks above no key
+    if (tid < (int)((8 - total % 8) % 8)) keys[total + tid] = 0;
+    lds_barrier();
+    const uint32_t n8 = (total + 7) / 8;
+    for (uint32_t i = tid; i < total; i += kSelThreads) {
+      const uint64_t mine = keys[i];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < n8; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rank += keys[8 * j + e] > mine ? 1u : 0u;
+      }
+      if (rank < (uint32_t)a.k) {
+        a.ids[(int64_t)q * a.k + rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)mine);
+        a.scores[(int64_t)q * a.k + rank] = float_of((uint32_t)(mine >> 32));
+      }
+    }
+    if (tid >= (int)total && tid < a.k) {
+      a.ids[(int64_t)q * a.k + tid] = -1;
+      a.scores[(int64_t)q * a.k + tid] = -INFINITY;
+    }
+    return;
+  }
+  auto take = [&](uint64_t v, uint64_t thr) {
+    if (v >= thr) {
+      const uint32_t slot = atomicAdd(&fs.n_best, 1u);   // at most k keys pass
+      if (slot < (uint32_t)kMaxK) fs.best[slot] = v;
+    }
+  };
+  if (staged) {
+    const uint64_t thr = kth_largest<uint64_t>([&](auto fn) {
+      for (uint32_t i = tid; i < total; i += kSelThreads) fn(keys[i]);
+    }, total, a.k, fs.sh);
+    for (uint32_t i = tid; i < total; i += kSelThreads) take(keys[i], thr);
+  } else {
+    const uint64_t thr = kth_largest<uint64_t>(each, total, a.k, fs.sh);
+    each([&](uint64_t v) { take(v, thr); });
+  }
+  __syncthreads();
+  if (tid < 64) write(wave_sort_desc(fs.best[tid]));
+}
+
+// Query q's candidates from the stream scan's regions (thread t gathers
+// scan workgroup t's), then its selection.
+__device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.scan_wgs;
-  // thread t gathers the region of scan workgroup t
   const uint32_t cnt = tid < G ? a.count[(int64_t)q * kTopkMaxScanWG + tid] : 0u;
   uint32_t incl = cnt;
 #pragma unroll
@@ -921,25 +1013,20 @@ __device__ void final_query(const TopkLaunch& a, int q, FinalShared& fs) {
     const uint32_t o = __shfl_up(incl, off);
     if (lane >= off) incl += o;
   }
-  if (lane == 63) wtot[wave] = incl;
-  if (tid < kMaxK) best[tid] = 0;
-  if (tid == 0) n_best = 0;
+  if (lane == 63) fs.wtot[wave] = incl;
+  if (tid < kMaxK) fs.best[tid] = 0;
+  if (tid == 0) fs.n_best = 0;
   __syncthreads();
   uint32_t excl = incl - cnt, total = 0;
   for (int w2 = 0; w2 < kSelThreads / 64; ++w2) {
-    if (w2 < wave) excl += wtot[w2];
-    total += wtot[w2];
+    if (w2 < wave) excl += fs.wtot[w2];
+    total += fs.wtot[w2];
   }
   const uint64_t* mine =
       a.cand + (int64_t)q * a.cand_stride +
       (tid < G ? region_tile(tid, a.n_tiles, G) * a.scan_tile : 0);
-  auto take = [&](uint64_t v, uint64_t thr) {
-    if (v >= thr) {
-      const uint32_t slot = atomicAdd(&n_best, 1u);   // at most k keys pass
-      if (slot < (uint32_t)kMaxK) best[slot] = v;
-    }
-  };
-  if (total <= (uint32_t)kStage64) {
+  const bool staged = total <= (uint32_t)kStage64;
+  if (staged) {
     // eight independent loads in flight per thread
     for (uint32_t i0 = 0; i0 < cnt; i0 += 8) {
       uint64_t t[8];
@@ -947,40 +1034,135 @@ __device__ void final_query(const TopkLaunch& a, int q, FinalShared& fs) {
       for (int j = 0; j < 8; ++j) t[j] = i0 + j < cnt ? mine[i0 + j] : 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (i0 + j < cnt) keys[excl + i0 + j] = t[j];
+        if (i0 + j < cnt) fs.keys[excl + i0 + j] = t[j];
     }
     __syncthreads();
-    if (total <= 64) {
-      // few candidates (one request, small k): one wave sorts them all
-      if (tid < 64) {
-        const uint64_t v = wave_sort_desc(tid < (int)total ? keys[tid] : 0ull);
-        if (tid < a.k) {
-          a.ids[(int64_t)q * a.k + tid] = v ? (int32_t)(0xFFFFFFFFu - (uint32_t)v) : -1;
-          a.scores[(int64_t)q * a.k + tid] = v ? float_of((uint32_t)(v >> 32)) : -INFINITY;
+  }
+  select_best(a, q, fs, total, staged, [&](auto fn) {
+    for (uint32_t i = 0; i < cnt; ++i) fn(mine[i]);
+  });
+}
+
+// One-pass mode.  Thread t holds the maxima of groups t + 256 j (groups of
+// 16 facts, j < 32).  The bound is the k-th largest of the 256 threads'
+// maxima: k threads, hence k groups and k distinct facts, reach it, so the
+// query's k best are codes that reach it in groups whose maximum does --
+// about k groups, nearly all among the two best groups of some thread,
+// whose codes each thread loads while the bound is found.  Group g's 16
+// codes are facts 32 (g / 2) + 4 (g % 2) + 8 (e / 4) + e % 4, e = 0 .. 15,
+// in the order the scan stored them.
+__device__ void final_dense(const TopkLaunch& a, int q, FinalShared& fs) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t ng = a.n_groups;   // <= kDenseGroups
+  const uint32_t* gm = a.gmax + (int64_t)q * ng;
+  const uint32_t* codes = a.codes + (int64_t)q * a.code_stride;
+  constexpr int kJ = kDenseGroups / kSelThreads;
+  uint32_t gv[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int64_t i = tid + (int64_t)kSelThreads * j;
+    gv[j] = i < ng ? gm[i] : 0u;
+  }
+  // this thread's two best groups (j1, j2; maxima m1 >= m2)
+  uint32_t m1 = 0, m2 = 0;
+  int j1 = 0, j2 = 0;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const uint32_t v = gv[j];
+    if (v > m1) {
+      m2 = m1;
+      j2 = j1;
+      m1 = v;
+      j1 = j;
+    } else if (v > m2) {
+      m2 = v;
+      j2 = j;
+    }
+  }
+  // the codes of group tid + 256 j; returns the group's first fact
+  auto load_group = [&](int j, u32x4 (&c)[4]) -> uint32_t {
+    const int64_t g = tid + (int64_t)kSelThreads * j;
+    const u32x4* src = reinterpret_cast<const u32x4*>(codes + g * 16);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) c[h] = src[h];
+    return (uint32_t)(32 * (g >> 1) + 4 * (g & 1));
+  };
+  u32x4 c1[4], c2[4];   // on their way while the bound is found
+  const uint32_t f1 = m1 != 0u ? load_group(j1, c1) : 0u;
+  const uint32_t f2 = m2 != 0u ? load_group(j2, c2) : 0u;
+  fs.vals[tid] = m1;
+  if (tid < kMaxK) fs.best[tid] = 0;
+  if (tid == 0) {
+    fs.n_best = 0;
+    fs.n_cand = 0;
+  }
+  lds_barrier();
+  // rank of this thread's maximum among the 256; the bound is the least
+  // maximum ranked below k (0 when fewer than k threads hold a group:
+  // then every group holds candidates)
+  uint32_t above = 0;
+  const u32x4* v4 = reinterpret_cast<const u32x4*>(fs.vals);
+#pragma unroll 8
+  for (int i = 0; i < kSelThreads / 4; ++i) {
+    const u32x4 v = v4[i];
+    above += (v[0] > m1 ? 1u : 0u) + (v[1] > m1 ? 1u : 0u) + (v[2] > m1 ? 1u : 0u) +
+             (v[3] > m1 ? 1u : 0u);
+  }
+  uint32_t t = above < (uint32_t)a.k ? m1 : 0xFFFFFFFFu;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)t, off);
+    t = o < t ? o : t;
+  }
+  if (lane == 0) fs.wtot[wave] = t;
+  lds_barrier();   // the maxima are dead; the keys take their place
+#pragma unroll
+  for (int w2 = 0; w2 < kSelThreads / 64; ++w2) t = fs.wtot[w2] < t ? fs.wtot[w2] : t;
+  auto reaches = [&](uint32_t c) { return c != 0u && c >= t; };
+  uint32_t mask = 0;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) mask |= reaches(gv[j]) ? 1u << j : 0u;
+  auto append = [&](const u32x4 (&c)[4], uint32_t f0) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) n += reaches(c[h][i]) ? 1u : 0u;
+    uint32_t slot = atomicAdd(&fs.n_cand, n);   // the group's share of the key list
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (reaches(c[h][i])) {
+          if (slot < (uint32_t)kStage64) fs.keys[slot] = key_of(c[h][i], f0 + 8 * h + i);
+          ++slot;
         }
-      }
-      return;
-    }
-    const uint64_t thr = kth_largest<uint64_t>([&](auto fn) {
-      for (uint32_t i = tid; i < total; i += kSelThreads) fn(keys[i]);
-    }, total, a.k, sh);
-    for (uint32_t i = tid; i < total; i += kSelThreads) take(keys[i], thr);
-  } else {
-    const uint64_t thr = kth_largest<uint64_t>([&](auto fn) {
-      for (uint32_t i = 0; i < cnt; ++i) fn(mine[i]);
-    }, total, a.k, sh);
-    for (uint32_t i = 0; i < cnt; ++i) take(mine[i], thr);
+  };
+  if (reaches(m1)) append(c1, f1);
+  if (reaches(m2)) append(c2, f2);
+  for (uint32_t m = mask & ~(1u << j1) & ~(m2 != 0u ? 1u << j2 : 0u); m != 0; m &= m - 1) {
+    u32x4 c[4];
+    const uint32_t f0 = load_group(__builtin_ctz(m), c);
+    append(c, f0);
   }
-  __syncthreads();
-  if (tid < 64) {
-    const uint64_t v = wave_sort_desc(best[tid]);
-    if (tid < a.k) {
-      // key 0: fewer candidates than k (cannot happen for a consistent
-      // bound); reported as id -1, score -inf
-      a.ids[(int64_t)q * a.k + tid] = v ? (int32_t)(0xFFFFFFFFu - (uint32_t)v) : -1;
-      a.scores[(int64_t)q * a.k + tid] = v ? float_of((uint32_t)(v >> 32)) : -INFINITY;
+  lds_barrier();
+  const uint32_t total = fs.n_cand;
+  select_best(a, q, fs, total, total <= (uint32_t)kStage64, [&](auto fn) {
+    for (uint32_t m = mask; m != 0; m &= m - 1) {
+      u32x4 c[4];
+      const uint32_t f0 = load_group(__builtin_ctz(m), c);
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (reaches(c[h][i])) fn(key_of(c[h][i], f0 + 8 * h + i));
     }
-  }
+  });
+}
+
+__device__ void final_query(const TopkLaunch& a, int q, FinalShared& fs) {
+  if (a.dense) final_dense(a, q, fs);
+  else final_regions(a, q, fs);
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
@@ -989,11 +1171,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
 }
 
 // One request (one query): its final selection, then its composition by
-// the wave that wrote the ids (its own stores, in program order), so the
-// composer's launch drops out of the request's path.
+// the first wave once the barrier has made every thread's ids visible, so
+// the composer's launch drops out of the request's path.
 __global__ __launch_bounds__(kSelThreads) void topk_final_compose(TopkLaunch a, ComposeLaunch c) {
   __shared__ FinalShared fs;
   final_query(a, 0, fs);
+  __syncthreads();   // the ids are written by the threads that hold them
   if (threadIdx.x < 64) compose_request(c, 0, threadIdx.x);
 }
 
@@ -1162,12 +1345,30 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
       else hipLaunchKernelGGL((topk_scan<false, 4>), g, b, 0, stream, a);
     }
   };
-  // at most four queries on the shared tile: the stream finds the bounds
-  a.fuse_tau = shared && a.n_q <= kWaves && a.n_groups <= kWaveKthMax;
-  scan(true, (unsigned)sample_wgs);
-  if (!a.fuse_tau)
-    hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
-  scan(false, (unsigned)a.scan_wgs);
+  // One pass when the codes of every score are few: the scan writes them
+  // all with the maxima of all groups, and the final kernel takes the bound
+  // from those (no sample scan, no threshold launch).
+  const int64_t scanned = a.n_tiles * ft_stream;   // facts the stream scan covers
+  a.dense = (shared || resident) && scanned / 16 <= kDenseGroups &&
+            (int64_t)a.n_q * scanned <= (int64_t)IS_TOPK_DENSE_CODES;
+  if (a.dense) {
+    a.codes = reinterpret_cast<uint32_t*>(a.cand);   // n_q x scanned x 4.25 B <= the cand buffer
+    a.code_stride = scanned;
+    a.gmax = a.codes + (int64_t)a.n_q * scanned;
+    a.n_groups = scanned / 16;
+    a.fuse_tau = 0;
+    const dim3 g((unsigned)a.scan_wgs), b(kThreads);
+    if (shared) hipLaunchKernelGGL((topk_scan_rq<false, 128, true, true>), g, b, 0, stream, a);
+    else if (ft_stream == 64) hipLaunchKernelGGL((topk_scan_rq<false, 64, false, true>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((topk_scan_rq<false, 32, false, true>), g, b, 0, stream, a);
+  } else {
+    // at most four queries on the shared tile: the stream finds the bounds
+    a.fuse_tau = shared && a.n_q <= kWaves && a.n_groups <= kWaveKthMax;
+    scan(true, (unsigned)sample_wgs);
+    if (!a.fuse_tau)
+      hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
+    scan(false, (unsigned)a.scan_wgs);
+  }
   if (compose != nullptr && a.n_q == 1)
     hipLaunchKernelGGL(topk_final_compose, dim3(1), dim3(kSelThreads), 0, stream, a, *compose);
   else

@@ -291,19 +291,23 @@ def test_topk_ties_and_self_match(gpu):
         st.destroy()
 
 
-@pytest.mark.parametrize("n_q", [100, 20, 3])
-def test_topk_many_candidates_full_batch(gpu, n_q):
-    """A store where almost every fact shares one embedding: every fact of a
+@pytest.mark.parametrize("n_facts,n_q", [(140001, 100), (140001, 20), (140001, 3),
+                                         (30000, 100), (30000, 20), (30000, 3)])
+def test_topk_many_candidates_full_batch(gpu, n_facts, n_q):
+    """A store where almost every fact shares one embedding.  Equal scores go
+    to the lower ids.  140,001 facts (sample, bound, stream): every fact of a
     workgroup's tiles reaches the sample bound, so candidates overflow the
-    scan's staging area and the final selection gathers from the full list.
-    Equal scores go to the lower ids.  100 queries: one query tile per wave;
-    20: one tile shared by the waves, positions from the workgroup's counter;
-    3: the same, with the bound found inside the stream scan."""
-    w = W.WORKLOADS["tiny"].scaled(name="flat1024", n_facts=140001, emb_dim=1024, n_req=n_q,
+    scan's staging area and the final selection gathers from the full list;
+    100 queries: one query tile per wave; 20: one tile shared by the waves,
+    positions from the workgroup's counter; 3: the same, with the bound found
+    inside the stream scan.  30,000 facts (one pass): every group's maximum
+    is the shared score, so every group holds candidates, more than the
+    final kernel stages, and the selection reads them from the codes."""
+    w = W.WORKLOADS["tiny"].scaled(name="flat1024", n_facts=n_facts, emb_dim=1024, n_req=n_q,
                                    len_dist=("uniform", 1, 1))
     lens = W.fact_lengths(w)
     emb = W.fact_embeddings(w)
-    distinct = [3, 1000, 70000, 139999]
+    distinct = [3, 1000, n_facts // 2, n_facts - 2]
     common = emb[5].copy()
     keep_rows = emb[distinct].copy()
     emb[:] = common
@@ -324,15 +328,17 @@ def test_topk_many_candidates_full_batch(gpu, n_q):
         st.destroy()
 
 
-def test_topk_ties_full_batch_width_1024(gpu):
-    """Equal embeddings under the register-resident scan (100 queries x 1024):
-    equal scores are ordered by the lower id, a self-query ranks its copies
-    first."""
-    w = W.WORKLOADS["tiny"].scaled(name="ties1024", n_facts=140001, emb_dim=1024, n_req=100,
+@pytest.mark.parametrize("n_facts", [140001, 20000])
+def test_topk_ties_full_batch_width_1024(gpu, n_facts):
+    """Equal embeddings under the register-resident scan (100 queries x 1024;
+    140,001 facts: sample, bound and stream; 20,000: one pass): equal scores
+    are ordered by the lower id, a self-query ranks its copies first."""
+    w = W.WORKLOADS["tiny"].scaled(name="ties1024", n_facts=n_facts, emb_dim=1024, n_req=100,
                                    len_dist=("uniform", 1, 1))
     lens = W.fact_lengths(w)
     emb = W.fact_embeddings(w)
-    for dup in (300, 33000, 140000):
+    dups = [300, n_facts // 4, n_facts - 1]
+    for dup in dups:
         emb[dup] = emb[17]
     desc, keep = Hn.K.make_desc(1, 2, 64, synth.F32, lens, 1024, -1, None, None, emb)
     h = Hn.K.is_store_create(desc)
@@ -340,12 +346,38 @@ def test_topk_ties_full_batch_width_1024(gpu):
     try:
         q = W.query_embeddings(w)
         q[0] = emb[17]
-        q[99] = emb[140000]
-        q[50] = emb[139999]
+        q[99] = emb[n_facts - 1]
+        q[50] = emb[n_facts - 2]
         ids, sc = Hn.gpu_topk(st, q, 5)
-        assert ids[0, :4].tolist() == [17, 300, 33000, 140000]
-        assert ids[99, :4].tolist() == [17, 300, 33000, 140000]
-        assert ids[50, 0] == 139999
+        assert ids[0, :4].tolist() == [17] + dups
+        assert ids[99, :4].tolist() == [17] + dups
+        assert ids[50, 0] == n_facts - 2
         Hn.check_topk(q, st.emb, ids, sc, 5, queries=[0, 1, 50, 98, 99])
+    finally:
+        st.destroy()
+
+
+@pytest.mark.parametrize("n_q", [100, 1])
+def test_topk_one_pass_many_copies(gpu, n_q):
+    """One pass over 30,000 facts, 1,500 of them copies of fact 7: a query
+    equal to fact 7 has 1,501 candidates at its best score (more than the
+    final kernel ranks one by one, fewer than it stages), so the radix
+    select orders them -- the lowest ids first."""
+    w = W.WORKLOADS["tiny"].scaled(name="copies1024", n_facts=30000, emb_dim=1024, n_req=n_q,
+                                   len_dist=("uniform", 1, 1))
+    lens = W.fact_lengths(w)
+    emb = W.fact_embeddings(w)
+    rng = np.random.default_rng(11)
+    copies = np.sort(rng.choice(np.arange(8, 30000), size=1500, replace=False))
+    emb[copies] = emb[7]
+    desc, keep = Hn.K.make_desc(1, 2, 64, synth.F32, lens, 1024, -1, None, None, emb)
+    h = Hn.K.is_store_create(desc)
+    st = Hn.Store(w, lens, np.concatenate([[0], np.cumsum(lens)]), h, emb)
+    try:
+        q = W.query_embeddings(w)
+        q[0] = emb[7]
+        ids, sc = Hn.gpu_topk(st, q, 64)
+        assert ids[0].tolist() == [7] + copies[:63].tolist()
+        Hn.check_topk(q, st.emb, ids, sc, 64, queries=range(0, n_q, 11))
     finally:
         st.destroy()
