@@ -197,6 +197,25 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
+// Minimum over the wave: running minima within each row of 16 lanes
+// (row_shr 1, 2, 4, 8), then the rows chained (row_bcast15 into rows 1 and
+// 3, row_bcast31 into rows 2 and 3), so lane 63 holds the wave's; lanes a
+// shift leaves without a source keep their own value.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_min_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, kRowMask, 0xF, false);
+  return o < v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = dpp_min_step<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_min_step<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_min_step<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_min_step<0x118, 0xF>(v);   // row_shr:8
+  v = dpp_min_step<0x142, 0xA>(v);   // row_bcast:15
+  v = dpp_min_step<0x143, 0xC>(v);   // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Sorts the wave's 64 keys descending (bitonic network across lanes).
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t a) {
   const int lane = threadIdx.x & 63;
@@ -838,6 +857,7 @@ constexpr int kSelThreads = 256;
 constexpr int kStage32 = 8192;   // group maxima staged in LDS by the threshold kernel
 constexpr int kStage64 = 4096;   // candidate keys staged in LDS by the final kernel
 constexpr int kDenseGroups = 32 * kSelThreads;   // group maxima the one-pass final holds
+constexpr int kBestGroups = 2;   // groups per thread the one-pass final fetches ahead
 
 struct SelShared {
   uint32_t hist[256];
@@ -929,6 +949,7 @@ struct FinalShared {
   uint64_t best[kMaxK];
   uint32_t n_best;
   uint32_t n_cand;
+  int32_t gsel[kBestGroups * kSelThreads];   // one-pass mode: each thread's best groups
 };
 
 // Barrier over the workgroup's LDS accesses only: global loads in flight
@@ -1044,13 +1065,15 @@ __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
 }
 
 // One-pass mode.  Thread t holds the maxima of groups t + 256 j (groups of
-// 16 facts, j < 32).  The bound is the k-th largest of the 256 threads'
-// maxima: k threads, hence k groups and k distinct facts, reach it, so the
-// query's k best are codes that reach it in groups whose maximum does --
-// about k groups, nearly all among the two best groups of some thread,
-// whose codes each thread loads while the bound is found.  Group g's 16
-// codes are facts 32 (g / 2) + 4 (g % 2) + 8 (e / 4) + e % 4, e = 0 .. 15,
-// in the order the scan stored them.
+// 16 facts, j < 32).  The bound comes from the threads' best maxima (see
+// below); k groups, hence k distinct facts, reach it, so the query's k best
+// are codes that reach it in groups whose maximum does -- a few more than k
+// groups, nearly all among the two best groups of some thread.  Those
+// groups' codes are on their way while the bound is found, fetched four
+// lanes to a group (each lane 16 bytes, a quarter of the group) so that
+// one load instruction covers 16 whole groups.  Group g's 16 codes are facts
+// 32 (g / 2) + 4 (g % 2) + 8 (e / 4) + e % 4, e = 0 .. 15, in the order the
+// scan stored them.
 __device__ void final_dense(const TopkLaunch& a, int q, FinalShared& fs) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t ng = a.n_groups;   // <= kDenseGroups
@@ -1063,22 +1086,26 @@ __device__ void final_dense(const TopkLaunch& a, int q, FinalShared& fs) {
     const int64_t i = tid + (int64_t)kSelThreads * j;
     gv[j] = i < ng ? gm[i] : 0u;
   }
-  // this thread's two best groups (j1, j2; maxima m1 >= m2)
-  uint32_t m1 = 0, m2 = 0;
-  int j1 = 0, j2 = 0;
+  // this thread's best groups: jb[0..2], maxima mb[0] >= mb[1] >= mb[2]
+  // (0: none)
+  uint32_t mb[kBestGroups] = {};
+  int jb[kBestGroups] = {};
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
-    const uint32_t v = gv[j];
-    if (v > m1) {
-      m2 = m1;
-      j2 = j1;
-      m1 = v;
-      j1 = j;
-    } else if (v > m2) {
-      m2 = v;
-      j2 = j;
-    }
+    uint32_t v = gv[j];
+    int jj = j;
+#pragma unroll
+    for (int b = 0; b < kBestGroups; ++b)
+      if (v > mb[b]) {
+        const uint32_t tv = mb[b];
+        const int tj = jb[b];
+        mb[b] = v;
+        jb[b] = jj;
+        v = tv;
+        jj = tj;
+      }
   }
+  const uint32_t m1 = mb[0];
   // the codes of group tid + 256 j; returns the group's first fact
   auto load_group = [&](int j, u32x4 (&c)[4]) -> uint32_t {
     const int64_t g = tid + (int64_t)kSelThreads * j;
@@ -1087,33 +1114,48 @@ __device__ void final_dense(const TopkLaunch& a, int q, FinalShared& fs) {
     for (int h = 0; h < 4; ++h) c[h] = src[h];
     return (uint32_t)(32 * (g >> 1) + 4 * (g & 1));
   };
-  u32x4 c1[4], c2[4];   // on their way while the bound is found
-  const uint32_t f1 = m1 != 0u ? load_group(j1, c1) : 0u;
-  const uint32_t f2 = m2 != 0u ? load_group(j2, c2) : 0u;
+  // the wave's best groups (kBestGroups per thread; -1: none), exchanged
+  // through LDS within the wave (its own writes, in order), then lane l
+  // fetches quarter l % 4 of group slot 16 i + l / 4
+  constexpr int kSlots = 64 * kBestGroups;   // the wave's
+  constexpr int kPieces = kSlots * 4 / 64;   // per lane
+#pragma unroll
+  for (int b = 0; b < kBestGroups; ++b)
+    fs.gsel[kBestGroups * tid + b] = mb[b] != 0u ? tid + kSelThreads * jb[b] : -1;
+  u32x4 pc[kPieces];
+  uint32_t pf[kPieces];
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int g = fs.gsel[wave * kSlots + 16 * i + lane / 4];
+    const int h = lane % 4;
+    pc[i] = u32x4{0u, 0u, 0u, 0u};
+    pf[i] = 0u;
+    if (g >= 0) {
+      pc[i] = *reinterpret_cast<const u32x4*>(codes + (int64_t)g * 16 + 4 * h);
+      pf[i] = (uint32_t)(32 * (g >> 1) + 4 * (g & 1) + 8 * h);
+    }
+  }
   fs.vals[tid] = m1;
   if (tid < kMaxK) fs.best[tid] = 0;
   if (tid == 0) {
     fs.n_best = 0;
     fs.n_cand = 0;
   }
-  lds_barrier();
-  // rank of this thread's maximum among the 256; the bound is the least
-  // maximum ranked below k (0 when fewer than k threads hold a group:
-  // then every group holds candidates)
+  // Rank of this thread's maximum among its wave's 64 (the wave's own LDS
+  // writes, in order): the wave's bound is the least maximum ranked below
+  // ceil(k / 4), so each wave has that many maxima at or above it, and the
+  // least of the four wave bounds is reached by at least k maxima (0 when
+  // fewer threads hold a group: then every group holds candidates).
+  const uint32_t kw = (uint32_t)(a.k + kSelThreads / 64 - 1) / (kSelThreads / 64);
   uint32_t above = 0;
-  const u32x4* v4 = reinterpret_cast<const u32x4*>(fs.vals);
-#pragma unroll 8
-  for (int i = 0; i < kSelThreads / 4; ++i) {
+  const u32x4* v4 = reinterpret_cast<const u32x4*>(fs.vals + wave * 64);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
     const u32x4 v = v4[i];
     above += (v[0] > m1 ? 1u : 0u) + (v[1] > m1 ? 1u : 0u) + (v[2] > m1 ? 1u : 0u) +
              (v[3] > m1 ? 1u : 0u);
   }
-  uint32_t t = above < (uint32_t)a.k ? m1 : 0xFFFFFFFFu;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)t, off);
-    t = o < t ? o : t;
-  }
+  uint32_t t = wave_min_u32(above < kw ? m1 : 0xFFFFFFFFu);
   if (lane == 0) fs.wtot[wave] = t;
   lds_barrier();   // the maxima are dead; the keys take their place
 #pragma unroll
@@ -1138,9 +1180,31 @@ __device__ void final_dense(const TopkLaunch& a, int q, FinalShared& fs) {
           ++slot;
         }
   };
-  if (reaches(m1)) append(c1, f1);
-  if (reaches(m2)) append(c2, f2);
-  for (uint32_t m = mask & ~(1u << j1) & ~(m2 != 0u ? 1u << j2 : 0u); m != 0; m &= m - 1) {
+  {
+    // the fetched quarters: a code that reaches the bound lies in a group
+    // whose maximum does
+    uint32_t n = 0;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) n += reaches(pc[i][e]) ? 1u : 0u;
+    if (n != 0) {
+      uint32_t slot = atomicAdd(&fs.n_cand, n);
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (reaches(pc[i][e])) {
+            if (slot < (uint32_t)kStage64) fs.keys[slot] = key_of(pc[i][e], pf[i] + e);
+            ++slot;
+          }
+    }
+  }
+  // the rare qualifying groups past a thread's best ones
+  uint32_t fetched = 0;
+#pragma unroll
+  for (int b = 0; b < kBestGroups; ++b) fetched |= mb[b] != 0u ? 1u << jb[b] : 0u;
+  for (uint32_t m = mask & ~fetched; m != 0; m &= m - 1) {
     u32x4 c[4];
     const uint32_t f0 = load_group(__builtin_ctz(m), c);
     append(c, f0);
