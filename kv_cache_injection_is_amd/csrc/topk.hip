@@ -914,43 +914,7 @@ __device__ V kth_largest(Each each, int64_t n, int k, SelShared& sh) {
   return prefix;
 }
 
-// Per query: tau = the k-th largest group maximum of the sample (lowered by
-// a hair), or -inf when the sample has fewer than k non-empty groups.
-__global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
-  __shared__ uint32_t vals[kStage32];
-  __shared__ SelShared sh;
-  const int q = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int64_t n = a.n_groups;
-  const uint32_t* src = a.gmax + (int64_t)q * n;
-  uint32_t kth;
-  if (n <= kStage32) {
-    for (int64_t i = tid; i < n; i += kSelThreads) vals[i] = src[i];
-    __syncthreads();
-    kth = kth_largest<uint32_t>([&](auto fn) {
-      for (int64_t i = tid; i < n; i += kSelThreads) fn(vals[i]);
-    }, n, a.k, sh);
-  } else {
-    kth = kth_largest<uint32_t>([&](auto fn) {
-      for (int64_t i = tid; i < n; i += kSelThreads) fn(src[i]);
-    }, n, a.k, sh);
-  }
-  if (tid == 0) a.tau[q] = tau_of_code(kth);
-}
-
-// Per query: the k best candidates, in order.
-struct FinalShared {
-  union {
-    uint64_t keys[kStage64];   // candidate keys
-    uint32_t vals[kSelThreads];   // one-pass mode: each thread's largest group maximum
-  };
-  SelShared sh;
-  uint32_t wtot[kSelThreads / 64];
-  uint64_t best[kMaxK];
-  uint32_t n_best;
-  uint32_t n_cand;
-  int32_t gsel[kBestGroups * kSelThreads];   // one-pass mode: each thread's best groups
-};
+constexpr int kSel = 2 * kSelThreads;   // keys the final kernel orders by counting
 
 // Barrier over the workgroup's LDS accesses only: global loads in flight
 // (the one-pass final's prefetched codes) stay in flight across it.
@@ -958,11 +922,169 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// A bound reached by at least k codes of the workgroup: every thread
+// offers its largest code `mine` (0: none); each wave ranks its 64 offers
+// (its own lanes' LDS writes, read back in order) and keeps the least offer
+// ranked below ceil(k / 4), which that many of its offers reach, so the
+// least of the four waves' is reached by at least k offers -- k distinct
+// codes (0 when fewer threads offer one).  `offers` holds a code per
+// thread, `wmin` one per wave; one barrier.
+__device__ __forceinline__ uint32_t offer_bound(uint32_t mine, int k, uint32_t* offers, uint32_t* wmin) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  offers[tid] = mine;
+  const uint32_t kw = (uint32_t)(k + kSelThreads / 64 - 1) / (kSelThreads / 64);
+  uint32_t above = 0;
+  const u32x4* v4 = reinterpret_cast<const u32x4*>(offers + wave * 64);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const u32x4 v = v4[i];
+    above += (v[0] > mine ? 1u : 0u) + (v[1] > mine ? 1u : 0u) + (v[2] > mine ? 1u : 0u) +
+             (v[3] > mine ? 1u : 0u);
+  }
+  uint32_t t = wave_min_u32(above < kw ? mine : 0xFFFFFFFFu);
+  if (lane == 0) wmin[wave] = t;
+  lds_barrier();
+#pragma unroll
+  for (int w2 = 0; w2 < kSelThreads / 64; ++w2) t = wmin[w2] < t ? wmin[w2] : t;
+  return t;
+}
+
+// Per query: tau = the k-th largest group maximum of the sample (lowered by
+// a hair), or -inf when the sample has fewer than k non-empty groups.  Up
+// to kDenseGroups maxima (32 per thread): the maxima that reach a bound k of
+// them reach (offer_bound) hold the k-th largest, with its rank among all,
+// so it is the least of them ranked below k; many equal maxima, or more
+// groups, take the radix select.
+__global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
+  __shared__ uint32_t vals[kStage32];
+  __shared__ SelShared sh;
+  __shared__ __attribute__((aligned(16))) uint32_t offers[kSelThreads];
+  __shared__ uint32_t wmin[kSelThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t sel[kSel];
+  __shared__ uint32_t n_sel;
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t n = a.n_groups;
+  const uint32_t* src = a.gmax + (int64_t)q * n;
+  uint32_t kth = 0;
+  bool done = false;
+  if (n <= kDenseGroups && n >= a.k) {
+    constexpr int kJ = kDenseGroups / kSelThreads;
+    uint32_t v[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int64_t i = tid + (int64_t)kSelThreads * j;
+      v[j] = i < n ? src[i] : 0u;
+    }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) mx = v[j] > mx ? v[j] : mx;
+    if (tid == 0) n_sel = 0;
+    for (int i = tid; i < kSel; i += kSelThreads) sel[i] = 0;   // past the selection: zero
+    const uint32_t t1 = offer_bound(mx, a.k, offers, wmin);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) cnt += (v[j] != 0u && v[j] >= t1) ? 1u : 0u;
+    if (cnt != 0) {
+      uint32_t slot = atomicAdd(&n_sel, cnt);
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+        if (v[j] != 0u && v[j] >= t1) {
+          if (slot < (uint32_t)kSel) sel[slot] = v[j];
+          ++slot;
+        }
+    }
+    lds_barrier();
+    const uint32_t m = n_sel;
+    if (m <= (uint32_t)kSel) {
+      // fewer than k nonzero maxima: the k-th largest is an empty group (0)
+      uint32_t least = 0xFFFFFFFFu;
+      if (m >= (uint32_t)a.k) {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(sel);
+        for (uint32_t i = tid; i < m; i += kSelThreads) {
+          const uint32_t mine = sel[i];
+          uint32_t above = 0;
+          for (uint32_t j = 0; j < (m + 3) / 4; ++j) {
+            const u32x4 w4 = s4[j];
+            above += (w4[0] > mine ? 1u : 0u) + (w4[1] > mine ? 1u : 0u) +
+                     (w4[2] > mine ? 1u : 0u) + (w4[3] > mine ? 1u : 0u);
+          }
+          if (above < (uint32_t)a.k && mine < least) least = mine;
+        }
+      }
+      least = wave_min_u32(least);
+      if ((tid & 63) == 0) wmin[tid >> 6] = least;   // each wave read wmin before the last barrier
+      lds_barrier();
+#pragma unroll
+      for (int w2 = 0; w2 < kSelThreads / 64; ++w2) least = wmin[w2] < least ? wmin[w2] : least;
+      kth = m >= (uint32_t)a.k ? least : 0u;
+      done = true;
+    }
+  }
+  if (!done) {
+    if (n <= kStage32) {
+      for (int64_t i = tid; i < n; i += kSelThreads) vals[i] = src[i];
+      __syncthreads();
+      kth = kth_largest<uint32_t>([&](auto fn) {
+        for (int64_t i = tid; i < n; i += kSelThreads) fn(vals[i]);
+      }, n, a.k, sh);
+    } else {
+      kth = kth_largest<uint32_t>([&](auto fn) {
+        for (int64_t i = tid; i < n; i += kSelThreads) fn(src[i]);
+      }, n, a.k, sh);
+    }
+  }
+  if (tid == 0) a.tau[q] = tau_of_code(kth);
+}
+
+// Per query: the k best candidates, in order.
+struct FinalShared {
+  alignas(16) uint64_t keys[kStage64];   // candidate keys
+  alignas(16) uint64_t sel[kSel + 8];    // the candidates that reach a bound (room for padding)
+  SelShared sh;
+  alignas(16) uint32_t offers[kSelThreads];   // read 16 bytes at a time
+  uint32_t wtot[kSelThreads / 64];
+  uint64_t best[kMaxK];
+  uint32_t n_best;
+  uint32_t n_cand;
+  uint32_t n_sel;
+  int32_t gsel[kBestGroups * kSelThreads];   // one-pass mode: each thread's best groups
+};
+
+// Query q's k best of the m distinct keys set[0, m) (m <= kSel), written
+// in order: every key counts the keys above it, which is its position.
+// Positions past m (fewer than k keys: cannot happen for a consistent
+// bound) are id -1, score -inf.  Pads set[m, m rounded up to 8) with zero
+// keys, which rank above none; one barrier.
+__device__ __forceinline__ void write_ranked(const TopkLaunch& a, int q, uint64_t* set, uint32_t m) {
+  const int tid = threadIdx.x;
+  if (tid < (int)((8 - m % 8) % 8)) set[m + tid] = 0;
+  lds_barrier();
+  const uint32_t n8 = (m + 7) / 8;
+  for (uint32_t i = tid; i < m; i += kSelThreads) {
+    const uint64_t mine = set[i];
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < n8; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rank += set[8 * j + e] > mine ? 1u : 0u;
+    }
+    if (rank < (uint32_t)a.k) {
+      a.ids[(int64_t)q * a.k + rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)mine);
+      a.scores[(int64_t)q * a.k + rank] = float_of((uint32_t)(mine >> 32));
+    }
+  }
+  if (tid >= (int)m && tid < a.k) {
+    a.ids[(int64_t)q * a.k + tid] = -1;
+    a.scores[(int64_t)q * a.k + tid] = -INFINITY;
+  }
+}
+
 // The k best of `total` candidate keys, as query q's ids and scores (the
-// threads of the workgroup that hold them write them).  `staged`: the keys sit in
-// fs.keys[0, total); otherwise each(fn) hands fn every key this thread
-// owns, read from memory.  fs.best and fs.n_best are cleared, and a barrier
-// has passed since.
+// threads of the workgroup that hold them write them).  `staged`: the keys
+// sit in fs.keys[0, total); otherwise each(fn) hands fn every key this
+// thread owns, read from memory.  fs.best, fs.n_best and fs.n_sel are
+// cleared, and a barrier has passed since.  Many equal scores fall through
+// to the radix select.
 template <typename Each>
 __device__ void select_best(const TopkLaunch& a, int q, FinalShared& fs, uint32_t total,
                             bool staged, Each each) {
@@ -976,32 +1098,27 @@ __device__ void select_best(const TopkLaunch& a, int q, FinalShared& fs, uint32_
       a.scores[(int64_t)q * a.k + tid] = v ? float_of((uint32_t)(v >> 32)) : -INFINITY;
     }
   };
-  if (staged && total <= 2 * kSelThreads) {
-    // a few hundred at most: every key counts the keys above it (the keys
-    // are distinct, so the counts are the final positions); positions past
-    // the candidates (fewer than k: cannot happen for a consistent bound)
-    // are reported as id -1, score -inf
-    // keys [total, total rounded up to 8) are zero, which ranks above no key
-    if (tid < (int)((8 - total % 8) % 8)) keys[total + tid] = 0;
-    lds_barrier();
-    const uint32_t n8 = (total + 7) / 8;
-    for (uint32_t i = tid; i < total; i += kSelThreads) {
-      const uint64_t mine = keys[i];
-      uint32_t rank = 0;
-      for (uint32_t j = 0; j < n8; ++j) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rank += keys[8 * j + e] > mine ? 1u : 0u;
-      }
-      if (rank < (uint32_t)a.k) {
-        a.ids[(int64_t)q * a.k + rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)mine);
-        a.scores[(int64_t)q * a.k + rank] = float_of((uint32_t)(mine >> 32));
-      }
-    }
-    if (tid >= (int)total && tid < a.k) {
-      a.ids[(int64_t)q * a.k + tid] = -1;
-      a.scores[(int64_t)q * a.k + tid] = -INFINITY;
-    }
+  if (staged && total <= (uint32_t)kSel) {
+    write_ranked(a, q, keys, total);
     return;
+  }
+  if (staged) {
+    // the keys whose score reaches a bound that k of them reach hold the
+    // k best, with their positions among all the candidates
+    uint64_t mx = 0;
+    for (uint32_t i = tid; i < total; i += kSelThreads) mx = keys[i] > mx ? keys[i] : mx;
+    const uint32_t t1 = offer_bound((uint32_t)(mx >> 32), a.k, fs.offers, fs.wtot);
+    for (uint32_t i = tid; i < total; i += kSelThreads)
+      if ((uint32_t)(keys[i] >> 32) >= t1) {
+        const uint32_t slot = atomicAdd(&fs.n_sel, 1u);
+        if (slot < (uint32_t)kSel) fs.sel[slot] = keys[i];
+      }
+    lds_barrier();
+    const uint32_t m = fs.n_sel;
+    if (m <= (uint32_t)kSel) {
+      write_ranked(a, q, fs.sel, m);
+      return;
+    }
   }
   auto take = [&](uint64_t v, uint64_t thr) {
     if (v >= thr) {
@@ -1036,7 +1153,10 @@ __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
   }
   if (lane == 63) fs.wtot[wave] = incl;
   if (tid < kMaxK) fs.best[tid] = 0;
-  if (tid == 0) fs.n_best = 0;
+  if (tid == 0) {
+    fs.n_best = 0;
+    fs.n_sel = 0;
+  }
   __syncthreads();
   uint32_t excl = incl - cnt, total = 0;
   for (int w2 = 0; w2 < kSelThreads / 64; ++w2) {
@@ -1135,31 +1255,14 @@ __device__ void final_dense(const TopkLaunch& a, int q, FinalShared& fs) {
       pf[i] = (uint32_t)(32 * (g >> 1) + 4 * (g & 1) + 8 * h);
     }
   }
-  fs.vals[tid] = m1;
   if (tid < kMaxK) fs.best[tid] = 0;
   if (tid == 0) {
     fs.n_best = 0;
     fs.n_cand = 0;
+    fs.n_sel = 0;
   }
-  // Rank of this thread's maximum among its wave's 64 (the wave's own LDS
-  // writes, in order): the wave's bound is the least maximum ranked below
-  // ceil(k / 4), so each wave has that many maxima at or above it, and the
-  // least of the four wave bounds is reached by at least k maxima (0 when
-  // fewer threads hold a group: then every group holds candidates).
-  const uint32_t kw = (uint32_t)(a.k + kSelThreads / 64 - 1) / (kSelThreads / 64);
-  uint32_t above = 0;
-  const u32x4* v4 = reinterpret_cast<const u32x4*>(fs.vals + wave * 64);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const u32x4 v = v4[i];
-    above += (v[0] > m1 ? 1u : 0u) + (v[1] > m1 ? 1u : 0u) + (v[2] > m1 ? 1u : 0u) +
-             (v[3] > m1 ? 1u : 0u);
-  }
-  uint32_t t = wave_min_u32(above < kw ? m1 : 0xFFFFFFFFu);
-  if (lane == 0) fs.wtot[wave] = t;
-  lds_barrier();   // the maxima are dead; the keys take their place
-#pragma unroll
-  for (int w2 = 0; w2 < kSelThreads / 64; ++w2) t = fs.wtot[w2] < t ? fs.wtot[w2] : t;
+  // the bound: k groups reach it (0: every group holds candidates)
+  const uint32_t t = offer_bound(m1, a.k, fs.offers, fs.wtot);
   auto reaches = [&](uint32_t c) { return c != 0u && c >= t; };
   uint32_t mask = 0;
 #pragma unroll
@@ -1224,22 +1327,22 @@ __device__ void final_dense(const TopkLaunch& a, int q, FinalShared& fs) {
   });
 }
 
-__device__ void final_query(const TopkLaunch& a, int q, FinalShared& fs) {
-  if (a.dense) final_dense(a, q, fs);
-  else final_regions(a, q, fs);
-}
-
+// One kernel per mode, so that each holds only its own code.
+template <bool kDense>
 __global__ __launch_bounds__(kSelThreads) void topk_final(TopkLaunch a) {
   __shared__ FinalShared fs;
-  final_query(a, blockIdx.x, fs);
+  if (kDense) final_dense(a, blockIdx.x, fs);
+  else final_regions(a, blockIdx.x, fs);
 }
 
 // One request (one query): its final selection, then its composition by
 // the first wave once the barrier has made every thread's ids visible, so
 // the composer's launch drops out of the request's path.
+template <bool kDense>
 __global__ __launch_bounds__(kSelThreads) void topk_final_compose(TopkLaunch a, ComposeLaunch c) {
   __shared__ FinalShared fs;
-  final_query(a, 0, fs);
+  if (kDense) final_dense(a, 0, fs);
+  else final_regions(a, 0, fs);
   __syncthreads();   // the ids are written by the threads that hold them
   if (threadIdx.x < 64) compose_request(c, 0, threadIdx.x);
 }
@@ -1433,10 +1536,14 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
       hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
     scan(false, (unsigned)a.scan_wgs);
   }
-  if (compose != nullptr && a.n_q == 1)
-    hipLaunchKernelGGL(topk_final_compose, dim3(1), dim3(kSelThreads), 0, stream, a, *compose);
-  else
-    hipLaunchKernelGGL(topk_final, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);
+  const dim3 fb(kSelThreads);
+  if (compose != nullptr && a.n_q == 1) {
+    if (a.dense) hipLaunchKernelGGL(topk_final_compose<true>, dim3(1), fb, 0, stream, a, *compose);
+    else hipLaunchKernelGGL(topk_final_compose<false>, dim3(1), fb, 0, stream, a, *compose);
+  } else {
+    if (a.dense) hipLaunchKernelGGL(topk_final<true>, dim3((unsigned)a.n_q), fb, 0, stream, a);
+    else hipLaunchKernelGGL(topk_final<false>, dim3((unsigned)a.n_q), fb, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
