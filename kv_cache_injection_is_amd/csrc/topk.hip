@@ -69,9 +69,6 @@
 #endif                         // faster on the 50k and the 1M index)
 static_assert(IS_TOPK_STREAM_FT == 32 || IS_TOPK_STREAM_FT == 64,
               "stream tiles of 32 or 64 facts (128-fact tiles spill with the fragment prefetch)");
-#ifndef IS_TOPK_SAMPLE_WGS
-#define IS_TOPK_SAMPLE_WGS 192   // workgroups the sample scan should at least fill
-#endif
 #ifndef IS_TOPK_DENSE_CODES
 #define IS_TOPK_DENSE_CODES (1 << 23)   // most score codes (queries x facts) the one-pass
 #endif                                  // mode writes; 0 turns it off
@@ -1451,11 +1448,11 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
   TopkLaunch a = in;
   const int32_t padded = topk_padded_dim(a.emb_dim);
   // query tiles of 32 the launch fills: 1, 2 or 4.  At width 1024, full
-  // batches keep their queries in registers: the stream in 32-fact tiles,
-  // the sample in 64-fact tiles when that still gives it IS_TOPK_SAMPLE_WGS
-  // workgroups, else 32.  Batches of at most 32 queries share one query
-  // tile across the waves (128-fact tiles).  Other batches and widths use
-  // the staged scan.
+  // batches keep their queries in registers, sample and stream in 32-fact
+  // tiles (IS_TOPK_STREAM_FT for the stream; 64-fact sample tiles measured
+  // about 10% slower on the 1M index).  Batches of at most 32 queries share
+  // one query tile across the waves (128-fact tiles).  Other batches and
+  // widths use the staged scan.
   const int qt = a.n_q <= 32 ? 1 : a.n_q <= 64 ? 2 : 4;
   const bool wide = IS_TOPK_RESIDENT && padded == kRChunks * kKC;
   const bool resident = wide && qt == 4;
@@ -1467,11 +1464,6 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
   } else if (resident) {
     ft_stream = IS_TOPK_STREAM_FT;
     ft_sample = 32;
-    for (int f : {64})
-      if ((a.sample_n + f - 1) / f >= IS_TOPK_SAMPLE_WGS) {
-        ft_sample = f;
-        break;
-      }
   }
   a.scan_tile = ft_stream;
   a.sample_tile = ft_sample;
@@ -1496,8 +1488,7 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
       else hipLaunchKernelGGL((topk_scan_rq<false, 128, true>), g, b, 0, stream, a);
     } else if (resident) {
       if (sample) {
-        if (ft == 64) hipLaunchKernelGGL((topk_scan_rq<true, 64, false>), g, b, 0, stream, a);
-        else hipLaunchKernelGGL((topk_scan_rq<true, 32, false>), g, b, 0, stream, a);
+        hipLaunchKernelGGL((topk_scan_rq<true, 32, false>), g, b, 0, stream, a);
       } else {
         if (ft == 64) hipLaunchKernelGGL((topk_scan_rq<false, 64, false>), g, b, 0, stream, a);
         else hipLaunchKernelGGL((topk_scan_rq<false, 32, false>), g, b, 0, stream, a);
