@@ -40,16 +40,27 @@ __device__ inline bool compose_mark(uint64_t* bits, int64_t b0, int64_t b1) {
 }
 
 // Request r, by the calling wave (lane = its lane).  The first request's
-// wave also copies the rotation speeds to their device buffer.
+// wave also copies the rotation speeds to their device buffer.  Loads that
+// do not depend on each other are issued together: the prefix with the
+// ids, a fact's length and block addresses together, and the block-table
+// entries from the prefix's block on (lane i: entry b0 + i) before the
+// lengths are summed, so a request costs three memory round trips and the
+// slot marks.
 __device__ inline void compose_request(const ComposeLaunch& a, int r, int lane) {
   if (r == 0)
     for (int i = lane; i < a.n_pairs; i += 64) a.g_out[i] = a.g[i];
+  const int64_t P = a.prefix[r];
   const bool mine = lane < a.k;
   const int32_t f = mine ? a.ids[(int64_t)r * a.k + lane] : 0;
   const bool id_ok = f >= 0 && (int64_t)f < a.n_facts;
+  const int64_t len = (mine && id_ok) ? a.lens[f] : 0;
+  const uint64_t fk = (mine && id_ok) ? a.k_addr[f] : 0, fv = (mine && id_ok) ? a.v_addr[f] : 0;
+  const int64_t B = a.block_size;
+  const int32_t* bt = a.bt + (int64_t)r * a.max_blocks;
+  const int64_t b0 = P >= 0 ? P / B : 0;
+  const int32_t blk0 = b0 + lane < a.max_blocks ? bt[b0 + lane] : -1;   // the segment's first 64 blocks
   if (mine && !id_ok) compose_record(a.status, IS_ERR_FACT_ID);
   if (mine && id_ok && a.work_tmp != nullptr) atomicAdd(&a.buckets[compose_bucket_of(f, a.n_facts, a.n_hbm)], 1u);
-  const int64_t len = (mine && id_ok) ? a.lens[f] : 0;
   // inclusive scan of the lengths across the wave
   int64_t incl = len;
 #pragma unroll
@@ -62,7 +73,6 @@ __device__ inline void compose_request(const ComposeLaunch& a, int r, int lane) 
   const int lo_t = __shfl((int)(uint32_t)incl, 63);
   const int hi_t = __shfl((int)(uint32_t)(incl >> 32), 63);
   const int64_t T = (int64_t)(((uint64_t)(uint32_t)hi_t << 32) | (uint32_t)lo_t);
-  const int64_t P = a.prefix[r];
   if (P < 0) {
     if (lane == 0) compose_record(a.status, IS_ERR_INVALID_ARG);
     return;
@@ -73,8 +83,8 @@ __device__ inline void compose_request(const ComposeLaunch& a, int r, int lane) 
   }
   if (mine && id_ok) {
     WorkItem w;
-    w.k = a.k_addr[f];
-    w.v = a.v_addr[f];
+    w.k = fk;
+    w.v = fv;
     w.len = (int32_t)len;
     w.pos = (int32_t)(P + incl - len);
     w.req = r;
@@ -82,15 +92,13 @@ __device__ inline void compose_request(const ComposeLaunch& a, int r, int lane) 
     (a.work_tmp ? a.work_tmp : a.work)[(int64_t)r * a.k + lane] = w;
   }
   if (T == 0) return;
-  const int64_t B = a.block_size;
-  const int64_t b0 = P / B, b1 = (P + T - 1) / B;
+  const int64_t b1 = (P + T - 1) / B;
   if (b1 >= a.max_blocks) {
     if (lane == 0) compose_record(a.status, IS_ERR_BLOCK_TABLE);
     return;
   }
-  const int32_t* bt = a.bt + (int64_t)r * a.max_blocks;
   for (int64_t b = b0 + lane; b <= b1; b += 64) {
-    const int32_t blk = bt[b];
+    const int32_t blk = b - b0 < 64 ? blk0 : bt[b];
     if (blk < 0 || (int64_t)blk >= a.n_blocks) {
       compose_record(a.status, IS_ERR_BLOCK_TABLE);
       continue;
