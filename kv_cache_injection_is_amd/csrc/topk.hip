@@ -1045,6 +1045,7 @@ struct FinalShared {
   uint32_t n_best;
   uint32_t n_cand;
   uint32_t n_sel;
+  uint32_t roff[kTopkMaxScanWG + 1];   // first key of each scan workgroup's region
   int32_t gsel[kBestGroups * kSelThreads];   // one-pass mode: each thread's best groups
 };
 
@@ -1136,8 +1137,12 @@ __device__ void select_best(const TopkLaunch& a, int q, FinalShared& fs, uint32_
   if (tid < 64) write(wave_sort_desc(fs.best[tid]));
 }
 
-// Query q's candidates from the stream scan's regions (thread t gathers
-// scan workgroup t's), then its selection.
+// Query q's candidates from the stream scan's regions, then its selection.
+// Staged: key i of the concatenated regions is gathered by thread i % 256,
+// which finds its region among the regions' starts (the last start at or
+// before i), eight loads in flight per thread, so a few long regions (a
+// small store's one or two workgroups) cost one round trip; otherwise
+// thread t reads scan workgroup t's region from memory in each pass.
 __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.scan_wgs;
@@ -1165,14 +1170,30 @@ __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
       (tid < G ? region_tile(tid, a.n_tiles, G) * a.scan_tile : 0);
   const bool staged = total <= (uint32_t)kStage64;
   if (staged) {
-    // eight independent loads in flight per thread
-    for (uint32_t i0 = 0; i0 < cnt; i0 += 8) {
+    if (tid < G) fs.roff[tid] = excl;
+    lds_barrier();
+    const uint64_t* cq = a.cand + (int64_t)q * a.cand_stride;
+    for (uint32_t i0 = 0; i0 < total; i0 += 8 * kSelThreads) {
       uint64_t t[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t[j] = i0 + j < cnt ? mine[i0 + j] : 0;
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = i0 + tid + j * kSelThreads;
+        t[j] = 0;
+        if (i < total) {
+          int lo = 0, hi = G;   // roff[lo] <= i < roff[hi] (roff[G] standing for total)
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (fs.roff[mid] <= i) lo = mid;
+            else hi = mid;
+          }
+          t[j] = cq[region_tile(lo, a.n_tiles, G) * a.scan_tile + (i - fs.roff[lo])];
+        }
+      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (i0 + j < cnt) fs.keys[excl + i0 + j] = t[j];
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = i0 + tid + j * kSelThreads;
+        if (i < total) fs.keys[i] = t[j];
+      }
     }
     __syncthreads();
   }
