@@ -26,7 +26,7 @@
 //      directly).  For one request of a retrieve-and-inject call the final
 //      kernel then composes the request.
 // Small stores take one pass instead (at most 8M scores for the launch and
-// 131,072 facts, width 1024): the scan writes every fact's score as an
+// 131,072 facts, any width): the scan writes every fact's score as an
 // order code together with every group's maximum, and the final kernel
 // takes the bound from all the groups -- the k-th largest of its threads'
 // best group maxima -- then gathers the codes that reach it from the
@@ -304,11 +304,12 @@ __device__ __forceinline__ void mma_chunk(const u32x4* es, const u32x4* qs, int 
   }
 }
 
-template <bool kSample, int QT>
+template <bool kSample, int QT, bool kDense = false>
 __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
+  static_assert(!(kSample && kDense), "the one-pass scan is a stream scan");
   constexpr int kQDma = q_dma<QT>();
   __shared__ ScanSmem sm;
-  if (kSample) side_zero(a);
+  if (kSample || kDense) side_zero(a);
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int q = qt * 32 + row;
-    tau[qt] = (!kSample && q < a.n_q) ? a.tau[q] : 0.f;
+    tau[qt] = (!kSample && !kDense && q < a.n_q) ? a.tau[q] : 0.f;
   }
   if (tid < kQB) sm.count[tid] = 0;   // first read after the loop's barriers
   const uint64_t region0 = (uint64_t)region_tile(w, n_tiles, G) * kFT;
@@ -390,10 +391,22 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
         float mx = v[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
-        if (kSample) {
+        if (kSample || kDense) {
           if (q < a.n_q) {
             const int64_t gi = ((t * kWaves + wave) * 2 + ft) * 2 + grp;
             a.gmax[(int64_t)q * a.n_groups + gi] = (mx == -INFINITY) ? 0u : ord_of(mx);
+            if (kDense) {
+              // the group's 16 codes, in fragment order (0: padding)
+              u32x4* dst = reinterpret_cast<u32x4*>(a.codes + (int64_t)q * a.code_stride + gi * 16);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                u32x4 c;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  c[i] = v[4 * j + i] == -INFINITY ? 0u : ord_of(v[4 * j + i]);
+                dst[j] = c;
+              }
+            }
           }
         } else if (q < a.n_q && mx >= tau[qt]) {
           uint32_t m = 0;
@@ -445,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
     if (++cb == kStages) cb = 0;
   }
   wait_vm<0>();
-  if (!kSample) {
+  if (!kSample && !kDense) {
     __syncthreads();
     if (tid < a.n_q) a.count[(int64_t)tid * kTopkMaxScanWG + w] = sm.count[tid];
   }
@@ -1528,7 +1541,7 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
   // all with the maxima of all groups, and the final kernel takes the bound
   // from those (no sample scan, no threshold launch).
   const int64_t scanned = a.n_tiles * ft_stream;   // facts the stream scan covers
-  a.dense = (shared || resident) && scanned / 16 <= kDenseGroups &&
+  a.dense = scanned / 16 <= kDenseGroups &&
             (int64_t)a.n_q * scanned <= (int64_t)IS_TOPK_DENSE_CODES;
   if (a.dense) {
     a.codes = reinterpret_cast<uint32_t*>(a.cand);   // n_q x scanned x 4.25 B <= the cand buffer
@@ -1538,8 +1551,11 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
     a.fuse_tau = 0;
     const dim3 g((unsigned)a.scan_wgs), b(kThreads);
     if (shared) hipLaunchKernelGGL((topk_scan_rq<false, 128, true, true>), g, b, 0, stream, a);
-    else if (ft_stream == 64) hipLaunchKernelGGL((topk_scan_rq<false, 64, false, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((topk_scan_rq<false, 32, false, true>), g, b, 0, stream, a);
+    else if (resident && ft_stream == 64) hipLaunchKernelGGL((topk_scan_rq<false, 64, false, true>), g, b, 0, stream, a);
+    else if (resident) hipLaunchKernelGGL((topk_scan_rq<false, 32, false, true>), g, b, 0, stream, a);
+    else if (qt == 1) hipLaunchKernelGGL((topk_scan<false, 1, true>), g, b, 0, stream, a);
+    else if (qt == 2) hipLaunchKernelGGL((topk_scan<false, 2, true>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((topk_scan<false, 4, true>), g, b, 0, stream, a);
   } else {
     // at most four queries on the shared tile: the stream finds the bounds
     a.fuse_tau = shared && a.n_q <= kWaves && a.n_groups <= kWaveKthMax;

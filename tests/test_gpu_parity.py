@@ -255,6 +255,11 @@ def test_inject_invalid_call_writes_nothing(gpu):
     (20000, 1024, 4, 64),    # bound inside the stream scan, one query per wave
     (600000, 1024, 1, 9),    # shared query tile over a sample of 1,176 groups: the
                              # separate threshold kernel
+    (140001, 128, 3, 5),     # staged scan on a store past the one-pass limit (8,752
+                             # groups): sample, bound and stream, one query tile
+    (140001, 256, 40, 20),   # the same with two query tiles
+    (140001, 64, 100, 50),   # ... and four
+    (6000, 1024, 50, 30),    # 33-64 queries at width 1024: the staged scan, one pass
 ])
 def test_topk_parity(gpu, n_facts, dim, n_q, k):
     w = W.WORKLOADS["tiny"].scaled(name="topk", n_facts=n_facts, emb_dim=dim, n_req=n_q,
