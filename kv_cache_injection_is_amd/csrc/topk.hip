@@ -13,25 +13,29 @@
 //      (a few percent of the store) for every query; each lane reduces the
 //      16 scores it holds to their maximum, so the sample is cut into
 //      disjoint groups of 16 facts and each group reports its best score;
-//   2. threshold: per query, the k-th largest group maximum (radix select)
-//      is tau -- k groups, hence k distinct facts, reach it (for at most
-//      four queries on the shared query tile the stream scan finds it);
+//   2. threshold: per query, the k-th largest group maximum is tau -- k
+//      groups, hence k distinct facts, reach it (for at most four queries
+//      on the shared query tile the stream scan finds it);
 //   3. scan (stream mode): MFMA scores of all facts; a score >= tau is a
 //      candidate, appended to the workgroup's own region of the query's
 //      candidate list (position from LDS or from the query's own lanes, so
 //      the HBM stream is never drained to wait for a global atomic);
-//   4. final: per query, the candidate regions are gathered, the k-th
-//      largest (score, then lower id) key is found by radix select, and the
-//      k winners are sorted across a wave (at most 64 candidates: sorted
-//      directly).  For one request of a retrieve-and-inject call the final
-//      kernel then composes the request.
+//   4. final: per query, the candidate regions are gathered and the k best
+//      (score, then lower id) keys are placed by counting, for each key, the
+//      keys above it (after cutting many candidates down to those that reach
+//      a bound k of them reach).  For one request of a retrieve-and-inject
+//      call the final kernel then composes the request.
+// Steps 2 and 4 find their bounds the same way (offer_bound): each thread
+// offers its best value, each wave ranks its 64 offers, and the least of
+// the waves' ceil(k/4)-th best is reached by k offers; many equal values
+// fall through to a radix select.
 // Small stores take one pass instead (at most 8M scores for the launch and
 // 131,072 facts, any width): the scan writes every fact's score as an
 // order code together with every group's maximum, and the final kernel
-// takes the bound from all the groups -- the k-th largest of its threads'
-// best group maxima -- then gathers the codes that reach it from the
-// groups whose maximum does (about k groups).  No sample scan and no
-// threshold launch; the codes cost 4 bytes per (query, fact) of writes.
+// takes the bound from all the groups (offer_bound over its threads' best
+// group maxima), then gathers the codes that reach it from the groups whose
+// maximum does (a few more than k groups).  No sample scan and no threshold
+// launch; the codes cost 4 bytes per (query, fact) of writes.
 // Every scan computes a fact's score as the same MFMA chain, so a sample
 // fact scores identically in the sample and the stream, whatever the
 // variant or tile size, and a query scores alike alone or in a batch.
@@ -1237,7 +1241,7 @@ __device__ void final_dense(const TopkLaunch& a, int q, FinalShared& fs) {
     const int64_t i = tid + (int64_t)kSelThreads * j;
     gv[j] = i < ng ? gm[i] : 0u;
   }
-  // this thread's best groups: jb[0..2], maxima mb[0] >= mb[1] >= mb[2]
+  // this thread's best kBestGroups groups jb[], maxima mb[] descending
   // (0: none)
   uint32_t mb[kBestGroups] = {};
   int jb[kBestGroups] = {};
