@@ -929,6 +929,7 @@ __device__ V kth_largest(Each each, int64_t n, int k, SelShared& sh) {
 }
 
 constexpr int kSel = 2 * kSelThreads;   // keys the final kernel orders by counting
+constexpr int kFewRegions = 8;          // candidate regions the final gathers spread out
 
 // Barrier over the workgroup's LDS accesses only: global loads in flight
 // (the one-pass final's prefetched codes) stay in flight across it.
@@ -1062,7 +1063,8 @@ struct FinalShared {
   uint32_t n_best;
   uint32_t n_cand;
   uint32_t n_sel;
-  uint32_t roff[kTopkMaxScanWG + 1];   // first key of each scan workgroup's region
+  uint32_t roff[kFewRegions];      // few regions: the first key of each in the list
+  uint32_t rbase[kFewRegions];     // ... and its first fact (its offset in the candidate row)
   int32_t gsel[kBestGroups * kSelThreads];   // one-pass mode: each thread's best groups
 };
 
@@ -1155,11 +1157,11 @@ __device__ void select_best(const TopkLaunch& a, int q, FinalShared& fs, uint32_
 }
 
 // Query q's candidates from the stream scan's regions, then its selection.
-// Staged: key i of the concatenated regions is gathered by thread i % 256,
-// which finds its region among the regions' starts (the last start at or
-// before i), eight loads in flight per thread, so a few long regions (a
-// small store's one or two workgroups) cost one round trip; otherwise
-// thread t reads scan workgroup t's region from memory in each pass.
+// Staged: with at most kFewRegions regions (a small store's few scan
+// workgroups, each region long) the keys are spread over all threads, so
+// they cost one round trip; otherwise thread t loads region t, 16 keys in
+// flight (a large store's regions hold a few keys each).  Not staged:
+// thread t reads region t from memory in each pass.
 __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.scan_wgs;
@@ -1187,29 +1189,43 @@ __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
       (tid < G ? region_tile(tid, a.n_tiles, G) * a.scan_tile : 0);
   const bool staged = total <= (uint32_t)kStage64;
   if (staged) {
-    if (tid < G) fs.roff[tid] = excl;
-    lds_barrier();
-    const uint64_t* cq = a.cand + (int64_t)q * a.cand_stride;
-    for (uint32_t i0 = 0; i0 < total; i0 += 8 * kSelThreads) {
-      uint64_t t[8];
+    if (G <= kFewRegions) {
+      // a small store's few regions: key i of the concatenated regions is
+      // gathered by thread i % 256, which finds its region among the
+      // regions' starts (the last start at or before i), eight loads in
+      // flight per thread
+      if (tid < G) {
+        fs.roff[tid] = excl;
+        fs.rbase[tid] = (uint32_t)(region_tile(tid, a.n_tiles, G) * a.scan_tile);
+      }
+      lds_barrier();
+      const uint64_t* cq = a.cand + (int64_t)q * a.cand_stride;
+      for (uint32_t i0 = 0; i0 < total; i0 += 8 * kSelThreads) {
+        uint64_t t[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t i = i0 + tid + j * kSelThreads;
-        t[j] = 0;
-        if (i < total) {
-          int lo = 0, hi = G;   // roff[lo] <= i < roff[hi] (roff[G] standing for total)
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (fs.roff[mid] <= i) lo = mid;
-            else hi = mid;
-          }
-          t[j] = cq[region_tile(lo, a.n_tiles, G) * a.scan_tile + (i - fs.roff[lo])];
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t i = i0 + tid + j * kSelThreads;
+          int lo = 0;
+#pragma unroll
+          for (int step = kFewRegions / 2; step >= 1; step >>= 1)
+            if (lo + step < G && fs.roff[lo + step] <= i) lo += step;
+          t[j] = i < total ? cq[fs.rbase[lo] + (i - fs.roff[lo])] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t i = i0 + tid + j * kSelThreads;
+          if (i < total) fs.keys[i] = t[j];
         }
       }
+    } else {
+      // thread t loads scan workgroup t's region, 16 keys in flight
+      for (uint32_t i0 = 0; i0 < cnt; i0 += 16) {
+        uint64_t t[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t i = i0 + tid + j * kSelThreads;
-        if (i < total) fs.keys[i] = t[j];
+        for (int j = 0; j < 16; ++j) t[j] = i0 + j < cnt ? mine[i0 + j] : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (i0 + j < cnt) fs.keys[excl + i0 + j] = t[j];
       }
     }
     __syncthreads();
