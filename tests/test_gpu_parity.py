@@ -260,6 +260,9 @@ def test_inject_invalid_call_writes_nothing(gpu):
     (140001, 256, 40, 20),   # the same with two query tiles
     (140001, 64, 100, 50),   # ... and four
     (6000, 1024, 50, 30),    # 33-64 queries at width 1024: the staged scan, one pass
+    (131072, 1024, 1, 50),   # one pass at its limit: 8,192 groups, every thread of the
+                             # final holds 32 group maxima
+    (131100, 1024, 2, 7),    # just past it (8,200 groups): sample, bound and stream
 ])
 def test_topk_parity(gpu, n_facts, dim, n_q, k):
     w = W.WORKLOADS["tiny"].scaled(name="topk", n_facts=n_facts, emb_dim=dim, n_req=n_q,
