@@ -206,7 +206,7 @@ int is_topk(const is_store* s, const uint16_t* q_f16, int32_t n_q, int32_t k,
  * is_topk for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, results (bit for bit) and errors as is_topk, but the
- * call allocates nothing: its scratch is one fixed 72 MiB array in device
+ * call allocates nothing: its scratch is one fixed 80 MiB array in device
  * memory per GPU, held from the first call on that GPU until the process
  * ends, instead of the store's scratch ring.  Limit: stores of at most
  * 65,536 facts (larger stores: IS_ERR_UNSUPPORTED, nothing enqueued).

@@ -571,6 +571,8 @@ is::TopkLaunch topk_launch_of(const is_store* s, const uint16_t* q, int32_t q0, 
   a.gmax = reinterpret_cast<uint32_t*>(p + lay.gmax_off);
   a.tau = reinterpret_cast<float*>(p + lay.tau_off);
   a.count = reinterpret_cast<uint32_t*>(p + lay.count_off);
+  a.codes = reinterpret_cast<uint32_t*>(p + lay.scode_off);
+  a.scount = reinterpret_cast<uint32_t*>(p + lay.scount_off);
   a.cand = reinterpret_cast<uint64_t*>(p + lay.cand_off);
   a.ids = ids + (int64_t)q0 * k;
   a.scores = scores + (int64_t)q0 * k;
@@ -613,10 +615,10 @@ IS_EXPORT int is_topk(const is_store* cs, const uint16_t* q, int32_t n_q, int32_
 // device address comes from hipGetSymbolAddress, once per device, with that
 // device current.  Its size holds the largest scratch that the accepted
 // stores need: 128 queries x 65,536 facts of 8-byte candidate keys (64 MiB),
-// padded queries of the widest index (4 MiB) and the sample maxima, bounds
-// and counts.
+// padded queries of the widest index (4 MiB), the sample's score codes
+// (4 MiB) and the sample maxima, bounds and counts.
 constexpr int64_t kNoAllocMaxFacts = 65536;
-constexpr size_t kNoAllocScratchBytes = size_t(72) << 20;
+constexpr size_t kNoAllocScratchBytes = size_t(80) << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
@@ -653,10 +655,10 @@ IS_EXPORT int is_topk_noalloc(const is_store* cs, const uint16_t* q, int32_t n_q
   if (s->n_facts > kNoAllocMaxFacts)
     return fail(IS_ERR_UNSUPPORTED,
                 "is_topk_noalloc covers stores of at most 65,536 facts (its fixed scratch is "
-                "72 MiB per GPU); use is_topk");
+                "80 MiB per GPU); use is_topk");
   const is::TopkScratch lay = is::topk_scratch(s->n_facts, std::min<int32_t>(128, n_q), s->emb_dim);
   if (lay.bytes > kNoAllocScratchBytes)
-    return fail(IS_ERR_UNSUPPORTED, "the call's scratch exceeds the fixed 72 MiB");
+    return fail(IS_ERR_UNSUPPORTED, "the call's scratch exceeds the fixed 80 MiB");
   DeviceGuard guard(s->device);
   char* p = nullptr;
   rc = scratch_on_device(s->device, &p);

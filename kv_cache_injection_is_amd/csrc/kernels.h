@@ -126,15 +126,23 @@ struct TopkLaunch {
   int32_t scan_tile;      // facts per stream tile
   int32_t sample_tile;    // facts per sample tile
   int64_t n_tiles, sample_n, sample_tiles, n_groups, cand_stride;
+  // derived by launch_topk: the stream scan covers tiles [stream_t0,
+  // n_tiles).  stream_t0 > 0: the sample scan kept the codes of its facts
+  // (codes, below), which are the first stream_t0 tiles, and the threshold
+  // kernel put their candidates at the head of each candidate row
+  int64_t stream_t0;
   // scratch (see topk_scratch)
   uint16_t* q_pad;        // [n_q][padded_dim] when emb_dim % 64 != 0
   uint32_t* gmax;         // [n_q][n_groups] sample group maxima (order codes)
   float* tau;             // [n_q] bound on each query's k-th best score
   uint32_t* count;        // [n_q][kTopkMaxScanWG] candidates per scan workgroup
   uint64_t* cand;         // [n_q][cand_stride] candidate (score, id) keys
+  uint32_t* scount;       // [n_q] candidates of the sample's facts (stream_t0 > 0)
   // dense: the scan writes every fact's order code, grouped as the group
   // maxima are ([n_q][code_stride], in the cand buffer), and gmax holds the
-  // maxima of all n_groups groups (after the codes, same buffer)
+  // maxima of all n_groups groups (after the codes, same buffer).
+  // stream_t0 > 0: the sample scan writes its facts' codes the same way
+  // ([n_q][code_stride], a buffer of their own)
   uint32_t* codes;
   int64_t code_stride;
   int32_t* ids;           // [n_q][k]
@@ -162,7 +170,7 @@ int64_t topk_sample_size(int64_t n_facts);
 
 // Byte offsets of the scratch buffers of one call of n_q (<= 128) queries.
 struct TopkScratch {
-  size_t q_off, gmax_off, tau_off, count_off, cand_off, bytes;
+  size_t q_off, gmax_off, tau_off, count_off, scode_off, scount_off, cand_off, bytes;
 };
 TopkScratch topk_scratch(int64_t n_facts, int32_t n_q, int32_t emb_dim);
 // `compose` (one query only): the final kernel also composes and validates

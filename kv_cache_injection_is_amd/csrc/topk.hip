@@ -13,13 +13,18 @@
 //      (a few percent of the store) for every query; each lane reduces the
 //      16 scores it holds to their maximum, so the sample is cut into
 //      disjoint groups of 16 facts and each group reports its best score;
+//      the scan also keeps every sample score as a 4-byte order code;
 //   2. threshold: per query, the k-th largest group maximum is tau -- k
-//      groups, hence k distinct facts, reach it (for at most four queries
-//      on the shared query tile the stream scan finds it);
-//   3. scan (stream mode): MFMA scores of all facts; a score >= tau is a
-//      candidate, appended to the workgroup's own region of the query's
-//      candidate list (position from LDS or from the query's own lanes, so
-//      the HBM stream is never drained to wait for a global atomic);
+//      groups, hence k distinct facts, reach it -- and the sample's
+//      candidates (codes >= tau, from the groups whose maximum reaches it)
+//      go to the head of the query's candidate list (for at most four
+//      queries on the shared query tile the stream scan finds tau itself,
+//      over the whole store, and the sample keeps no codes);
+//   3. scan (stream mode): MFMA scores of the facts after the sample; a
+//      score >= tau is a candidate, appended to the workgroup's own region
+//      of the query's candidate list (position from LDS or from the query's
+//      own lanes, so the HBM stream is never drained to wait for a global
+//      atomic);
 //   4. final: per query, the candidate regions are gathered and the k best
 //      (score, then lower id) keys are placed by counting, for each key, the
 //      keys above it (after cutting many candidates down to those that reach
@@ -323,7 +328,9 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
   const int n_chunks = D / kKC;
   const int G = (int)gridDim.x;
   const int w = (int)blockIdx.x;
-  const int64_t n_tiles = kSample ? a.sample_tiles : a.n_tiles;
+  // the stream starts after the sample's tiles when the sample kept their codes
+  const int64_t t0 = kSample ? 0 : a.stream_t0;
+  const int64_t n_tiles = kSample ? a.sample_tiles : a.n_tiles - t0;
   const int my_tiles = (int)((n_tiles - w + G - 1) / G);
   const int total = my_tiles * n_chunks;
   const int64_t edge_tile = (a.n_facts - 1) / kFT;   // the tile that may hold padding rows
@@ -335,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
     tau[qt] = (!kSample && !kDense && q < a.n_q) ? a.tau[q] : 0.f;
   }
   if (tid < kQB) sm.count[tid] = 0;   // first read after the loop's barriers
-  const uint64_t region0 = (uint64_t)region_tile(w, n_tiles, G) * kFT;
+  const uint64_t region0 = (uint64_t)(t0 + region_tile(w, n_tiles, G)) * kFT;
 
   const uint32_t e_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.e[0][0];
   const uint32_t q_lds = (uint32_t)(size_t)(lds_cptr)(void*)&sm.q[0][0];
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
   // has finished with it; the query rows are read by every wave and wait for
   // the barrier.
   // Fact cursor: tile et, chunk ec, ring buffer eb.
-  int64_t et = w;
+  int64_t et = t0 + w;
   int ec = 0, eb = 0;
   auto issue_e = [&]() {
     // the tile's 256 x 64 block of the blocked layout: 32 KB contiguous
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
           if (q < a.n_q) {
             const int64_t gi = ((t * kWaves + wave) * 2 + ft) * 2 + grp;
             a.gmax[(int64_t)q * a.n_groups + gi] = (mx == -INFINITY) ? 0u : ord_of(mx);
-            if (kDense) {
+            if (kDense || a.stream_t0 > 0) {
               // the group's 16 codes, in fragment order (0: padding)
               u32x4* dst = reinterpret_cast<u32x4*>(a.codes + (int64_t)q * a.code_stride + gi * 16);
 #pragma unroll
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan(TopkLaunch a) {
     issue_q();
   }
   // Compute cursor: tile ct, chunk cc, ring buffer cb.
-  int64_t ct = w;
+  int64_t ct = t0 + w;
   int cc = 0, cb = 0;
   for (int g = 0; g < total; ++g) {
     // Chunk g+2's fact rows go into the buffer this wave finished with in
@@ -574,7 +581,9 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   const int grp = lane / 32;
   const int G = (int)gridDim.x;
   const int w = (int)blockIdx.x;
-  const int64_t n_tiles = kSample ? a.sample_tiles : a.n_tiles;
+  // the stream starts after the sample's tiles when the sample kept their codes
+  const int64_t t0 = kSample ? 0 : a.stream_t0;
+  const int64_t n_tiles = kSample ? a.sample_tiles : a.n_tiles - t0;
   const int my_tiles = (int)((n_tiles - w + G - 1) / G);
   const int64_t edge_tile = (a.n_facts - 1) / FT;
   const int q = (kShared ? 0 : wave * 32) + row;   // this lane's query (column of every score tile)
@@ -583,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   // queries, shared query tile) found below by wave q from the sample
   const bool fuse = kShared && !kSample && !kDense && a.fuse_tau;
   float tau = (!kSample && !kDense && !fuse && q_ok) ? a.tau[q] : 0.f;
-  const uint64_t region0 = (uint64_t)region_tile(w, n_tiles, G) * FT;
+  const uint64_t region0 = (uint64_t)(t0 + region_tile(w, n_tiles, G)) * FT;
   const bool stage_ok = (int64_t)my_tiles * FT <= ((int64_t)1 << kPosBits);
   uint32_t q_count = 0;    // candidates of this lane's query so far (both its lanes)
   uint32_t staged = 0;     // this wave's staging slots used (wave-uniform)
@@ -602,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   // Issue cursor: tile et (in FT-fact tiles), chunk ec.  Tile et is part
   // et % P of stored 256-fact tile et / P, whose chunk ec is one 32 KB span.
   constexpr int P = kFT / FT;
-  int64_t et = w;
+  int64_t et = t0 + w;
   int ec = 0;
   auto issue = [&](int slot_stage) {
     const uint16_t* blk =
@@ -641,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
         if (q_ok) {
           const int64_t gi = (t * R::kRows + ft) * 2 + grp;
           a.gmax[(int64_t)q * a.n_groups + gi] = (mx == -INFINITY) ? 0u : ord_of(mx);
-          if (kDense) {
+          if (kDense || a.stream_t0 > 0) {
             // the group's 16 codes, in fragment order (0: padding)
             u32x4* dst = reinterpret_cast<u32x4*>(a.codes + (int64_t)q * a.code_stride + gi * 16);
 #pragma unroll
@@ -825,7 +834,7 @@ __global__ __launch_bounds__(kThreads) void topk_scan_rq(TopkLaunch a) {
   ring_barrier();
   if (fuse && q_ok) tau = sm.qtau[row];
   read_frags(0, av);
-  int64_t ct = w;
+  int64_t ct = t0 + w;
   if constexpr (!kSample && !kShared && !kDense) {
     for (int i = 0; i + 1 < my_tiles; ++i) {
 #pragma unroll
@@ -970,38 +979,102 @@ __device__ __forceinline__ uint32_t offer_bound(uint32_t mine, int k, uint32_t* 
 // them reach (offer_bound) hold the k-th largest, with its rank among all,
 // so it is the least of them ranked below k; many equal maxima, or more
 // groups, take the radix select.
+// When the sample kept its facts' codes (stream_t0 > 0) the stream scan
+// skips those facts, and this kernel takes their candidates instead: the
+// codes that reach tau, from the groups whose maximum does (about k
+// groups), written at the head of the query's candidate row, their number
+// in scount.  Each thread's two best groups are fetched while tau is found.
 __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
-  __shared__ uint32_t vals[kStage32];
+  __shared__ __attribute__((aligned(16))) uint32_t vals[kStage32];
   __shared__ SelShared sh;
   __shared__ __attribute__((aligned(16))) uint32_t offers[kSelThreads];
   __shared__ uint32_t wmin[kSelThreads / 64];
   __shared__ __attribute__((aligned(16))) uint32_t sel[kSel];
   __shared__ uint32_t n_sel;
+  __shared__ uint32_t n_sc;    // the sample's candidates taken so far
+  __shared__ uint32_t n_grp;   // ... their groups listed so far
+  constexpr int kKeyStage = 1024;
+  __shared__ __attribute__((aligned(16))) uint64_t kstage[kKeyStage];   // their keys
+  __shared__ uint32_t glist[kStage32 / 16];                             // their groups
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t n = a.n_groups;
   const uint32_t* src = a.gmax + (int64_t)q * n;
+  const bool keep = a.stream_t0 > 0;
+  const u32x4* codes =
+      keep ? reinterpret_cast<const u32x4*>(a.codes + (int64_t)q * a.code_stride) : nullptr;
+  if (tid == 0) {
+    n_sc = 0;
+    n_grp = 0;
+  }
   uint32_t kth = 0;
   bool done = false;
-  if (n <= kDenseGroups && n >= a.k) {
-    constexpr int kJ = kDenseGroups / kSelThreads;
-    uint32_t v[kJ];
+  const bool fast = n <= kDenseGroups && n >= a.k;
+  constexpr int kJ = kDenseGroups / kSelThreads;
+  // fast: this thread's maxima (groups tid + 256 j) and its kPre best,
+  // whose codes are fetched into cp while the bound is ranked (of the k or
+  // so groups that reach it, a thread rarely holds more than two; kPre = 4
+  // leaves a dependent load after the bound to almost no launch).
+  constexpr int kPre = 4;
+  uint32_t v[kJ];
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const int64_t i = tid + (int64_t)kSelThreads * j;
-      v[j] = i < n ? src[i] : 0u;
+  for (int j = 0; j < kJ; ++j) {
+    const int64_t i = tid + (int64_t)kSelThreads * j;
+    v[j] = fast && i < n ? src[i] : 0u;
+  }
+  int bj[kPre];        // the best groups' j, best first (-1: none)
+  uint32_t bm[kPre];   // ... and their maxima
+#pragma unroll
+  for (int r = 0; r < kPre; ++r) {
+    bj[r] = -1;
+    bm[r] = 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    // insert v[j] into the descending list (ties keep the earlier j first)
+    uint32_t x = v[j];
+    int xj = j;
+#pragma unroll
+    for (int r = 0; r < kPre; ++r) {
+      const bool up = x > bm[r];
+      const uint32_t tm = bm[r];
+      const int tj = bj[r];
+      bm[r] = up ? x : tm;
+      bj[r] = up ? xj : tj;
+      x = up ? tm : x;
+      xj = up ? tj : xj;
     }
-    uint32_t mx = 0;
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) mx = v[j] > mx ? v[j] : mx;
+  }
+  const uint32_t mx = bm[0];
+  u32x4 cp[kPre][4];
+  uint32_t pf = 0;   // bit r: cp[r] holds group bj[r]'s codes
+  if (fast) {
     if (tid == 0) n_sel = 0;
     for (int i = tid; i < kSel; i += kSelThreads) sel[i] = 0;   // past the selection: zero
     const uint32_t t1 = offer_bound(mx, a.k, offers, wmin);
+    // The groups that reach t1 (at most kSel of them, about k) hold those
+    // that reach tau, but for a hair: their codes are fetched now, while
+    // the bound is ranked.  Every lane loads (a lane with nothing to fetch
+    // reads group 0, one line for all of them).
+    const u32x4* cbase = keep ? codes : reinterpret_cast<const u32x4*>(a.gmax);
+#pragma unroll
+    for (int r = 0; r < kPre; ++r) {
+      const bool want = keep && bj[r] >= 0 && bm[r] >= t1;
+      pf |= want ? 1u << r : 0u;
+      const int64_t g = want ? tid + (int64_t)kSelThreads * bj[r] : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cp[r][i] = cbase[g * 4 + i];
+    }
     uint32_t cnt = 0;
 #pragma unroll
     for (int j = 0; j < kJ; ++j) cnt += (v[j] != 0u && v[j] >= t1) ? 1u : 0u;
-    if (cnt != 0) {
-      uint32_t slot = atomicAdd(&n_sel, cnt);
+    {
+      // positions by a wave prefix sum, one LDS atomic per wave
+      uint32_t wave_n;
+      const uint32_t pre = wave_prefix(cnt, wave_n);
+      uint32_t base = 0;
+      if ((tid & 63) == 0 && wave_n != 0) base = atomicAdd(&n_sel, wave_n);
+      uint32_t slot = (uint32_t)__shfl((int)base, 0) + pre;
 #pragma unroll
       for (int j = 0; j < kJ; ++j)
         if (v[j] != 0u && v[j] >= t1) {
@@ -1015,14 +1088,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
       // fewer than k nonzero maxima: the k-th largest is an empty group (0)
       uint32_t least = 0xFFFFFFFFu;
       if (m >= (uint32_t)a.k) {
+        // eight 16-byte reads in flight; sel is zero past m (ranks above none)
         const u32x4* s4 = reinterpret_cast<const u32x4*>(sel);
+        const uint32_t n4 = ((m + 3) / 4 + 7) & ~7u;   // <= kSel / 4
         for (uint32_t i = tid; i < m; i += kSelThreads) {
           const uint32_t mine = sel[i];
           uint32_t above = 0;
-          for (uint32_t j = 0; j < (m + 3) / 4; ++j) {
-            const u32x4 w4 = s4[j];
-            above += (w4[0] > mine ? 1u : 0u) + (w4[1] > mine ? 1u : 0u) +
-                     (w4[2] > mine ? 1u : 0u) + (w4[3] > mine ? 1u : 0u);
+          for (uint32_t j0 = 0; j0 < n4; j0 += 8) {
+            u32x4 w4[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w4[u] = s4[j0 + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              above += (w4[u][0] > mine ? 1u : 0u) + (w4[u][1] > mine ? 1u : 0u) +
+                       (w4[u][2] > mine ? 1u : 0u) + (w4[u][3] > mine ? 1u : 0u);
           }
           if (above < (uint32_t)a.k && mine < least) least = mine;
         }
@@ -1049,7 +1128,128 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
       }, n, a.k, sh);
     }
   }
-  if (tid == 0) a.tau[q] = tau_of_code(kth);
+  const float tau = tau_of_code(kth);
+  if (tid == 0) a.tau[q] = tau;
+  if (!keep) return;
+  // The sample's candidates: group g's code e is fact
+  // 32 (g / 2) + 4 (g % 2) + 8 (e / 4) + e % 4, in the order the scan stored
+  // them.  A thread's groups that reach tau are its np best (the test is
+  // monotone in the maximum), so the first min(np, kPre) are in registers.
+  // Their codes are listed in LDS (the maxima's staging area, free once tau
+  // is known), then every thread tests (group, code) pairs of the list and
+  // the hits are placed by ballot prefix sums, one LDS atomic per wave;
+  // keys are staged in LDS and written out together.  More groups than the
+  // list holds (many equal maxima): each thread takes its own groups.
+  uint64_t* head = a.cand + (int64_t)q * a.cand_stride;
+  const int lane = tid & 63;
+  auto pass = [&](uint32_t gm) { return gm != 0u && float_of(gm) >= tau; };
+  auto put = [&](uint32_t slot, uint64_t key) {
+    if (slot < (uint32_t)kKeyStage) kstage[slot] = key;
+    else head[slot] = key;
+  };
+  auto fact = [](int64_t g, int e) {
+    return (uint32_t)(32 * (g >> 1) + 4 * (g & 1) + 8 * (e >> 2) + (e & 3));
+  };
+  u32x4* lcodes = reinterpret_cast<u32x4*>(vals);   // group i's codes: lcodes[4 i .. 4 i + 4)
+  constexpr uint32_t kListGroups = kStage32 / 16;
+  uint32_t pm = 0;   // fast: this thread's groups that reach tau (bit j)
+  if (fast) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) pm |= pass(v[j]) ? 1u << j : 0u;
+    const uint32_t np = (uint32_t)__builtin_popcount(pm);
+    uint32_t wave_n;
+    const uint32_t pre = wave_prefix(np, wave_n);
+    uint32_t base = 0;
+    if (lane == 0 && wave_n != 0) base = atomicAdd(&n_grp, wave_n);
+    const uint32_t slot = (uint32_t)__shfl((int)base, 0) + pre;
+#pragma unroll
+    for (int r = 0; r < kPre; ++r) {
+      if ((uint32_t)r < np && slot + r < kListGroups) {
+        const int64_t g = tid + (int64_t)kSelThreads * bj[r];
+        if (pf & (1u << r)) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lcodes[(slot + r) * 4 + i] = cp[r][i];
+        } else {   // reaches tau, not t1 (within the hair below it)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lcodes[(slot + r) * 4 + i] = codes[g * 4 + i];
+        }
+        glist[slot + r] = (uint32_t)g;
+      }
+    }
+    if (np > (uint32_t)kPre) {
+      // groups past the fetched ones, in j order after them
+      uint32_t rest = pm;
+#pragma unroll
+      for (int r = 0; r < kPre; ++r) rest &= bj[r] >= 0 ? ~(1u << bj[r]) : ~0u;
+      uint32_t at = slot + kPre;
+      while (rest != 0) {
+        const int j = __builtin_ctz(rest);
+        rest &= rest - 1;
+        const int64_t g = tid + (int64_t)kSelThreads * j;
+        if (at < kListGroups) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lcodes[at * 4 + i] = codes[g * 4 + i];
+          glist[at] = (uint32_t)g;
+        }
+        ++at;
+      }
+    }
+  }
+  lds_barrier();   // the list and its length
+  const uint32_t n_list = n_grp;
+  if (fast && n_list <= kListGroups) {
+    const uint32_t* lc = vals;
+    const uint32_t pairs = 16 * n_list;
+    // four pairs per thread per round (uniform trip count), one prefix sum
+    // and one LDS atomic per wave per round
+    for (uint32_t p0 = 0; p0 < pairs; p0 += 4 * kSelThreads) {
+      uint32_t o[4], hits = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t p = p0 + tid + u * kSelThreads;
+        o[u] = p < pairs ? lc[p] : 0u;
+        hits |= (o[u] != 0u && float_of(o[u]) >= tau) ? 1u << u : 0u;
+      }
+      uint32_t wave_n;
+      const uint32_t pre = wave_prefix((uint32_t)__builtin_popcount(hits), wave_n);
+      uint32_t base = 0;
+      if (lane == 0 && wave_n != 0) base = atomicAdd(&n_sc, wave_n);
+      uint32_t slot = (uint32_t)__shfl((int)base, 0) + pre;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (hits & (1u << u)) {
+          const uint32_t p = p0 + tid + u * kSelThreads;
+          put(slot++, key_of(o[u], fact(glist[p >> 4], (int)(p & 15))));
+        }
+    }
+  } else {
+    // each thread its own groups that reach tau
+    auto take = [&](int64_t g, const u32x4 (&c)[4]) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t o = c[e / 4][e % 4];
+        m |= (o != 0u && float_of(o) >= tau) ? 1u << e : 0u;
+      }
+      if (m == 0) return;
+      uint32_t slot = atomicAdd(&n_sc, (uint32_t)__builtin_popcount(m));
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (m & (1u << e)) put(slot++, key_of(c[e / 4][e % 4], fact(g, e)));
+    };
+    for (int64_t g = tid; g < n; g += kSelThreads) {
+      if (!pass(src[g])) continue;
+      u32x4 c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = codes[g * 4 + i];
+      take(g, c);
+    }
+  }
+  __syncthreads();
+  const uint32_t total = n_sc;
+  const uint32_t in_lds = total < (uint32_t)kKeyStage ? total : (uint32_t)kKeyStage;
+  for (uint32_t i = tid; i < in_lds; i += kSelThreads) head[i] = kstage[i];
+  if (tid == 0) a.scount[q] = total;
 }
 
 // Per query: the k best candidates, in order.
@@ -1063,8 +1263,8 @@ struct FinalShared {
   uint32_t n_best;
   uint32_t n_cand;
   uint32_t n_sel;
-  uint32_t roff[kFewRegions];      // few regions: the first key of each in the list
-  uint32_t rbase[kFewRegions];     // ... and its first fact (its offset in the candidate row)
+  uint32_t roff[kFewRegions + 1];    // few regions: the first key of each in the list
+  uint32_t rbase[kFewRegions + 1];   // ... and its offset in the candidate row
   int32_t gsel[kBestGroups * kSelThreads];   // one-pass mode: each thread's best groups
 };
 
@@ -1156,15 +1356,21 @@ __device__ void select_best(const TopkLaunch& a, int q, FinalShared& fs, uint32_
   if (tid < 64) write(wave_sort_desc(fs.best[tid]));
 }
 
-// Query q's candidates from the stream scan's regions, then its selection.
-// Staged: with at most kFewRegions regions (a small store's few scan
-// workgroups, each region long) the keys are spread over all threads, so
-// they cost one round trip; otherwise thread t loads region t, 16 keys in
-// flight (a large store's regions hold a few keys each).  Not staged:
-// thread t reads region t from memory in each pass.
+// Query q's candidates from the stream scan's regions (and, when the
+// stream skipped the sample's facts, the threshold kernel's candidates of
+// those, at the head of the row), then its selection.  Staged: with at most
+// kFewRegions stream regions (a small store's few scan workgroups, each
+// region long) the keys are spread over all threads, so they cost one round
+// trip; otherwise thread t loads region t, 16 keys in flight (a large
+// store's regions hold a few keys each), and the head's keys are spread
+// over the threads.  Not staged: thread t reads region t and every 256th
+// key of the head from memory in each pass.
 __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.scan_wgs;
+  const int64_t t0 = a.stream_t0;      // the stream's first tile
+  const int64_t nt = a.n_tiles - t0;   // ... and its tiles
+  const uint32_t sc = t0 > 0 ? a.scount[q] : 0u;   // keys at the head of the row
   const uint32_t cnt = tid < G ? a.count[(int64_t)q * kTopkMaxScanWG + tid] : 0u;
   uint32_t incl = cnt;
 #pragma unroll
@@ -1179,27 +1385,31 @@ __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
     fs.n_sel = 0;
   }
   __syncthreads();
-  uint32_t excl = incl - cnt, total = 0;
+  // the list: the head's keys, then the regions' in workgroup order
+  uint32_t excl = sc + incl - cnt, total = sc;
   for (int w2 = 0; w2 < kSelThreads / 64; ++w2) {
     if (w2 < wave) excl += fs.wtot[w2];
     total += fs.wtot[w2];
   }
-  const uint64_t* mine =
-      a.cand + (int64_t)q * a.cand_stride +
-      (tid < G ? region_tile(tid, a.n_tiles, G) * a.scan_tile : 0);
+  const uint64_t* cq = a.cand + (int64_t)q * a.cand_stride;
+  const int64_t base = tid < G ? (t0 + region_tile(tid, nt, G)) * a.scan_tile : 0;
+  const uint64_t* mine = cq + base;
   const bool staged = total <= (uint32_t)kStage64;
   if (staged) {
     if (G <= kFewRegions) {
-      // a small store's few regions: key i of the concatenated regions is
-      // gathered by thread i % 256, which finds its region among the
-      // regions' starts (the last start at or before i), eight loads in
-      // flight per thread
+      // a small store's few regions (region 0 the head, r + 1 workgroup
+      // r's): key i of the list is gathered by thread i % 256, which finds
+      // its region among the regions' starts (the last start at or before
+      // i), eight loads in flight per thread
       if (tid < G) {
-        fs.roff[tid] = excl;
-        fs.rbase[tid] = (uint32_t)(region_tile(tid, a.n_tiles, G) * a.scan_tile);
+        fs.roff[tid + 1] = excl;
+        fs.rbase[tid + 1] = (uint32_t)base;
+      }
+      if (tid == 0) {
+        fs.roff[0] = 0;
+        fs.rbase[0] = 0;
       }
       lds_barrier();
-      const uint64_t* cq = a.cand + (int64_t)q * a.cand_stride;
       for (uint32_t i0 = 0; i0 < total; i0 += 8 * kSelThreads) {
         uint64_t t[8];
 #pragma unroll
@@ -1207,8 +1417,8 @@ __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
           const uint32_t i = i0 + tid + j * kSelThreads;
           int lo = 0;
 #pragma unroll
-          for (int step = kFewRegions / 2; step >= 1; step >>= 1)
-            if (lo + step < G && fs.roff[lo + step] <= i) lo += step;
+          for (int step = kFewRegions; step >= 1; step >>= 1)
+            if (lo + step <= G && fs.roff[lo + step] <= i) lo += step;
           t[j] = i < total ? cq[fs.rbase[lo] + (i - fs.roff[lo])] : 0;
         }
 #pragma unroll
@@ -1218,7 +1428,9 @@ __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
         }
       }
     } else {
-      // thread t loads scan workgroup t's region, 16 keys in flight
+      // the head's first 256 keys, one per thread, in flight with the
+      // regions': thread t loads scan workgroup t's region, 16 keys at a time
+      const uint64_t hk = (uint32_t)tid < sc ? cq[tid] : 0;
       for (uint32_t i0 = 0; i0 < cnt; i0 += 16) {
         uint64_t t[16];
 #pragma unroll
@@ -1227,10 +1439,13 @@ __device__ void final_regions(const TopkLaunch& a, int q, FinalShared& fs) {
         for (int j = 0; j < 16; ++j)
           if (i0 + j < cnt) fs.keys[excl + i0 + j] = t[j];
       }
+      if ((uint32_t)tid < sc) fs.keys[tid] = hk;
+      for (uint32_t i = tid + kSelThreads; i < sc; i += kSelThreads) fs.keys[i] = cq[i];
     }
     __syncthreads();
   }
   select_best(a, q, fs, total, staged, [&](auto fn) {
+    for (uint32_t i = tid; i < sc; i += kSelThreads) fn(cq[i]);
     for (uint32_t i = 0; i < cnt; ++i) fn(mine[i]);
   });
 }
@@ -1488,6 +1703,10 @@ TopkScratch topk_scratch(int64_t n_facts, int32_t n_q, int32_t emb_dim) {
   off += up((size_t)n_q * 4);
   s.count_off = off;
   off += up((size_t)n_q * kTopkMaxScanWG * 4);
+  s.scode_off = off;   // the sample's facts' codes (sample_tiles x sample_tile <= this width)
+  off += up((size_t)n_q * topk_padded_facts(topk_sample_size(n_facts)) * 4);
+  s.scount_off = off;
+  off += up((size_t)n_q * 4);
   s.cand_off = off;
   off += up((size_t)n_q * tiles * kFT * 8);
   s.bytes = off;
@@ -1500,6 +1719,7 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
       in.emb_dim % 8 != 0)
     return hipErrorInvalidValue;
   TopkLaunch a = in;
+  a.stream_t0 = 0;
   const int32_t padded = topk_padded_dim(a.emb_dim);
   // query tiles of 32 the launch fills: 1, 2 or 4.  At width 1024, full
   // batches keep their queries in registers, sample and stream in 32-fact
@@ -1579,6 +1799,17 @@ hipError_t launch_topk(const TopkLaunch& in, hipStream_t stream, const ComposeLa
   } else {
     // at most four queries on the shared tile: the stream finds the bounds
     a.fuse_tau = shared && a.n_q <= kWaves && a.n_groups <= kWaveKthMax;
+    // Otherwise the sample scan keeps its facts' codes, the threshold kernel
+    // takes their candidates from those, and the stream scan starts after
+    // the sample's tiles (the sample facts are whole stream tiles).
+    const int64_t sample_facts = a.sample_tiles * ft_sample;
+    if (!a.fuse_tau && a.codes != nullptr && a.scount != nullptr && sample_facts % ft_stream == 0 &&
+        sample_facts / ft_stream < a.n_tiles) {
+      a.stream_t0 = sample_facts / ft_stream;
+      a.code_stride = sample_facts;
+      const int64_t rest = a.n_tiles - a.stream_t0;
+      a.scan_wgs = (int32_t)(rest < kTopkMaxScanWG ? rest : kTopkMaxScanWG);
+    }
     scan(true, (unsigned)sample_wgs);
     if (!a.fuse_tau)
       hipLaunchKernelGGL(topk_threshold, dim3((unsigned)a.n_q), dim3(kSelThreads), 0, stream, a);

@@ -300,17 +300,21 @@ def test_topk_ties_and_self_match(gpu):
 
 
 @pytest.mark.parametrize("n_facts,n_q", [(140001, 100), (140001, 20), (140001, 3),
-                                         (30000, 100), (30000, 20), (30000, 3)])
+                                         (300000, 100), (30000, 100), (30000, 20), (30000, 3)])
 def test_topk_many_candidates_full_batch(gpu, n_facts, n_q):
     """A store where almost every fact shares one embedding.  Equal scores go
     to the lower ids.  140,001 facts (sample, bound, stream): every fact of a
     workgroup's tiles reaches the sample bound, so candidates overflow the
-    scan's staging area and the final selection gathers from the full list;
-    100 queries: one query tile per wave; 20: one tile shared by the waves,
-    positions from the workgroup's counter; 3: the same, with the bound found
-    inside the stream scan.  30,000 facts (one pass): every group's maximum
-    is the shared score, so every group holds candidates, more than the
-    final kernel stages, and the selection reads them from the codes."""
+    scan's staging area and the final selection gathers from the full list,
+    and every sample fact is a candidate that the threshold kernel takes
+    from the sample's codes (more keys than it stages); 100 queries: one
+    query tile per wave; 20: one tile shared by the waves, positions from
+    the workgroup's counter; 3: the same, with the bound found inside the
+    stream scan.  300,000 facts: 592 sample groups reach the bound, more
+    than the threshold kernel lists, so each of its threads takes its own.
+    30,000 facts (one pass): every group's maximum is the shared score, so
+    every group holds candidates, more than the final kernel stages, and the
+    selection reads them from the codes."""
     w = W.WORKLOADS["tiny"].scaled(name="flat1024", n_facts=n_facts, emb_dim=1024, n_req=n_q,
                                    len_dist=("uniform", 1, 1))
     lens = W.fact_lengths(w)
