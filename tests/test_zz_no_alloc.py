@@ -32,10 +32,12 @@ def _both(st, q_bits, k):
 
 
 def test_topk_noalloc_matches_topk(gpu):
-    # call 1: 60,000 facts at width 1024, 130 queries (two groups of the
-    # scratch, one after the other), k = 50
-    w1 = BASE.scaled(n_facts=60_000, emb_dim=1024)
-    Hn.log("no-alloc top-k: 60,000 facts x 1024, 130 queries, k=50")
+    # call 1: 65,536 facts (the largest store it takes) at width 1024, 130
+    # queries (two groups of the scratch, one after the other), k = 50; the
+    # first group's 8.4M scores take the sample, bound and stream, whose
+    # sample codes also live in the fixed scratch
+    w1 = BASE.scaled(n_facts=65_536, emb_dim=1024)
+    Hn.log("no-alloc top-k: 65,536 facts x 1024, 130 queries, k=50")
     st = Hn.make_store(w1)
     try:
         q1 = synth.queries(11, 130, 1024)
