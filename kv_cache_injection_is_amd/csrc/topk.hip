@@ -1016,11 +1016,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
   // so groups that reach it, a thread rarely holds more than two; kPre = 4
   // leaves a dependent load after the bound to almost no launch).
   constexpr int kPre = 4;
+  // Loops over a thread's maxima stop at jn, the count of 256-wide rows the
+  // groups fill (a uniform branch): at one wave per SIMD every instruction
+  // of these short kernels is on the critical path.
+  const int jn = fast ? (int)((n + kSelThreads - 1) / kSelThreads) : 0;
   uint32_t v[kJ];
 #pragma unroll
+  for (int j = 0; j < kJ; ++j) v[j] = 0u;
+#pragma unroll
   for (int j = 0; j < kJ; ++j) {
+    if (j >= jn) break;
     const int64_t i = tid + (int64_t)kSelThreads * j;
-    v[j] = fast && i < n ? src[i] : 0u;
+    v[j] = i < n ? src[i] : 0u;
   }
   int bj[kPre];        // the best groups' j, best first (-1: none)
   uint32_t bm[kPre];   // ... and their maxima
@@ -1031,6 +1038,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
   }
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
+    if (j >= jn) break;
     // insert v[j] into the descending list (ties keep the earlier j first)
     uint32_t x = v[j];
     int xj = j;
@@ -1067,7 +1075,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
     }
     uint32_t cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) cnt += (v[j] != 0u && v[j] >= t1) ? 1u : 0u;
+    for (int j = 0; j < kJ; ++j) {
+      if (j >= jn) break;
+      cnt += (v[j] != 0u && v[j] >= t1) ? 1u : 0u;
+    }
     {
       // positions by a wave prefix sum, one LDS atomic per wave
       uint32_t wave_n;
@@ -1076,11 +1087,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
       if ((tid & 63) == 0 && wave_n != 0) base = atomicAdd(&n_sel, wave_n);
       uint32_t slot = (uint32_t)__shfl((int)base, 0) + pre;
 #pragma unroll
-      for (int j = 0; j < kJ; ++j)
+      for (int j = 0; j < kJ; ++j) {
+        if (j >= jn) break;
         if (v[j] != 0u && v[j] >= t1) {
           if (slot < (uint32_t)kSel) sel[slot] = v[j];
           ++slot;
         }
+      }
     }
     lds_barrier();
     const uint32_t m = n_sel;
@@ -1155,7 +1168,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
   uint32_t pm = 0;   // fast: this thread's groups that reach tau (bit j)
   if (fast) {
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) pm |= pass(v[j]) ? 1u << j : 0u;
+    for (int j = 0; j < kJ; ++j) {
+      if (j >= jn) break;
+      pm |= pass(v[j]) ? 1u << j : 0u;
+    }
     const uint32_t np = (uint32_t)__builtin_popcount(pm);
     uint32_t wave_n;
     const uint32_t pre = wave_prefix(np, wave_n);
