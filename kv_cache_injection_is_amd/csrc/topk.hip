@@ -983,7 +983,8 @@ __device__ __forceinline__ uint32_t offer_bound(uint32_t mine, int k, uint32_t* 
 // skips those facts, and this kernel takes their candidates instead: the
 // codes that reach tau, from the groups whose maximum does (about k
 // groups), written at the head of the query's candidate row, their number
-// in scount.  Each thread's two best groups are fetched while tau is found.
+// in scount.  A thread's best groups that reach the first bound (up to four)
+// are fetched while the rest of the selection runs.
 __global__ __launch_bounds__(kSelThreads) void topk_threshold(TopkLaunch a) {
   __shared__ __attribute__((aligned(16))) uint32_t vals[kStage32];
   __shared__ SelShared sh;
